@@ -1,0 +1,221 @@
+"""CPU oracle for the ZeRO++ / LoCo block quantization and llm.c stochastic
+rounding path -- TEST INFRASTRUCTURE.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never does, and the
+two share no code: this wrapper marshals numpy arrays into the plain C oracle
+in ``zq_oracle.c`` (one element at a time, fp32 arithmetic exactly as the
+definitions state).  Each function below names the passage it follows; the C
+source holds the full statement.
+
+Host arrays only: fp32 data as ``np.float32``, bf16 data as ``np.uint16`` bit
+patterns, int4 codes as ``np.uint8`` (two per byte, low nibble first), int8
+codes as ``np.int8``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+# Output buffers start poisoned so that every byte the oracle returns was
+# written by it (an element it forgot shows up as 0xAA / NaN).
+_POISON_U8 = 0xAA
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = _build.ensure_built()
+        L = C.CDLL(path)
+        vp, sz, u32, f32, i32, u64 = C.c_void_p, C.c_size_t, C.c_uint32, C.c_float, C.c_int, C.c_uint64
+        L.orc_quant_block.argtypes = [vp, sz, i32, vp, vp]
+        L.orc_quant_block.restype = None
+        L.orc_int4_decode.argtypes = [vp, sz]
+        L.orc_int4_decode.restype = C.c_int32
+        L.orc_quantize_ef_int4.argtypes = [vp, i32, vp, sz, u32, f32, f32, vp, vp]
+        L.orc_quantize_ef_int4.restype = None
+        L.orc_dequant_reduce.argtypes = [u32, vp, vp, sz, u32, f32, vp, vp, vp, vp, f32, f32, vp]
+        L.orc_dequant_reduce.restype = None
+        L.orc_quant_int8.argtypes = [vp, i32, sz, u32, vp, vp]
+        L.orc_quant_int8.restype = None
+        L.orc_dequant_int8.argtypes = [vp, vp, sz, u32, vp, i32]
+        L.orc_dequant_int8.restype = None
+        L.orc_bf16_rne.argtypes = [f32]
+        L.orc_bf16_rne.restype = C.c_uint16
+        L.orc_philox4x32_10.argtypes = [vp, vp, vp]
+        L.orc_philox4x32_10.restype = None
+        L.orc_sr_r16.argtypes = [u64, u64]
+        L.orc_sr_r16.restype = u32
+        L.orc_sr_round.argtypes = [f32, u32]
+        L.orc_sr_round.restype = C.c_uint16
+        L.orc_sr_accumulate.argtypes = [vp, vp, sz, u64, u64, i32]
+        L.orc_sr_accumulate.restype = None
+        L.orc_sr_r16_fill.argtypes = [u64, u64, sz, vp]
+        L.orc_sr_r16_fill.restype = None
+        L.orc_volume_bytes.argtypes = [u64, u32, u32, vp]
+        L.orc_volume_bytes.restype = None
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be contiguous"
+    return a.ctypes.data
+
+
+def _check_block(block: int):
+    if block < 2 or block % 2 or block > 4096:
+        raise ValueError("oracle block must be even and in [2, 4096]")
+
+
+def int4_code_bytes(n: int) -> int:
+    return (n + 1) // 2
+
+
+def num_blocks(n: int, block: int) -> int:
+    return (n + block - 1) // block
+
+
+def quant_block(x: np.ndarray, qmax: int):
+    """Symmetric absmax quantizer of one block ([ZeRO++] notes, section 1.2:
+    block-based quantization).  Returns (codes int32[m], scale float32)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    k = np.empty(x.size, dtype=np.int32)
+    s = np.zeros(1, dtype=np.float32)
+    lib().orc_quant_block(_ptr(x), x.size, qmax, _ptr(k), _ptr(s))
+    return k, s[0]
+
+
+def int4_decode(codes: np.ndarray, n: int) -> np.ndarray:
+    """Signed int4 values of the first n elements of a packed code array."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    L = lib()
+    return np.array([L.orc_int4_decode(_ptr(codes), i) for i in range(n)], dtype=np.int32)
+
+
+def quantize_ef_int4(g: np.ndarray, ef: np.ndarray | None, block: int, beta_e: float,
+                     beta_r: float):
+    """LoCo error-feedback int4 quantize ("Merge LoCo with Zero++", Overview
+    and review thread).  g: float32 or uint16 (bf16 bits).  ef (float32) is
+    updated in place when given.  Returns (codes uint8[ceil(n/2)],
+    scales float32[ceil(n/block)])."""
+    _check_block(block)
+    g = np.ascontiguousarray(g)
+    if g.dtype == np.uint16:
+        is_bf16 = 1
+    elif g.dtype == np.float32:
+        is_bf16 = 0
+    else:
+        raise TypeError("g must be float32 or uint16 (bf16 bits)")
+    n = g.size
+    if ef is not None:
+        assert ef.dtype == np.float32 and ef.size == n and ef.flags["C_CONTIGUOUS"]
+    codes = np.full(int4_code_bytes(n), _POISON_U8, dtype=np.uint8)
+    scales = np.full(num_blocks(n, block), np.nan, dtype=np.float32)
+    lib().orc_quantize_ef_int4(_ptr(g), is_bf16, _ptr(ef), n, block, beta_e, beta_r,
+                               _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def dequant_reduce(codes_list, scales_list, n_chunk: int, block: int, alpha: float,
+                   want_out: bool = True, requant: bool = False, rq_ef: np.ndarray | None = None,
+                   rq_beta_e: float = 0.0, rq_beta_r: float = 1.0):
+    """qgZ receive side ([ZeRO++] notes, section 1.2): dequantize P int4
+    chunks and reduce in full precision, optionally requantize for the next
+    hierarchy level.  Returns (out or None, rq_codes or None, rq_scales or
+    None); rq_ef is updated in place when given."""
+    _check_block(block)
+    P = len(codes_list)
+    assert P == len(scales_list) and P >= 1
+    cl = [np.ascontiguousarray(c, dtype=np.uint8) for c in codes_list]
+    sl = [np.ascontiguousarray(s, dtype=np.float32) for s in scales_list]
+    cptr = (C.c_void_p * P)(*[c.ctypes.data for c in cl])
+    sptr = (C.c_void_p * P)(*[s.ctypes.data for s in sl])
+    out = np.full(n_chunk, np.nan, dtype=np.float32) if want_out else None
+    rq_codes = np.full(int4_code_bytes(n_chunk), _POISON_U8, dtype=np.uint8) if requant else None
+    rq_scales = np.full(num_blocks(n_chunk, block), np.nan, dtype=np.float32) if requant else None
+    work = np.empty(max(n_chunk, 1), dtype=np.float32)
+    if rq_ef is not None:
+        assert requant and rq_ef.dtype == np.float32 and rq_ef.size == n_chunk
+    lib().orc_dequant_reduce(P, cptr, sptr, n_chunk, block, alpha, _ptr(out), _ptr(rq_codes),
+                             _ptr(rq_scales), _ptr(rq_ef), rq_beta_e, rq_beta_r, _ptr(work))
+    return out, rq_codes, rq_scales
+
+
+def quant_int8(w: np.ndarray, block: int):
+    """qwZ int8 block quantization ([ZeRO++] notes, section 1.2).  w float32
+    or uint16 (bf16 bits).  Returns (codes int8[n], scales float32[nb])."""
+    _check_block(block)
+    w = np.ascontiguousarray(w)
+    is_bf16 = 1 if w.dtype == np.uint16 else 0
+    if not is_bf16 and w.dtype != np.float32:
+        raise TypeError("w must be float32 or uint16 (bf16 bits)")
+    codes = np.full(w.size, -86, dtype=np.int8)
+    scales = np.full(num_blocks(w.size, block), np.nan, dtype=np.float32)
+    lib().orc_quant_int8(_ptr(w), is_bf16, w.size, block, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def dequant_int8(codes: np.ndarray, scales: np.ndarray, block: int, out_bf16: bool):
+    """qwZ dequantize after the all-gather.  Returns float32[n] or uint16[n]
+    (bf16 bits, round to nearest even)."""
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    out = np.zeros(codes.size, dtype=np.uint16 if out_bf16 else np.float32)
+    lib().orc_dequant_int8(_ptr(codes), _ptr(scales), codes.size, block, _ptr(out),
+                           1 if out_bf16 else 0)
+    return out
+
+
+def bf16_rne(x: float) -> int:
+    return int(lib().orc_bf16_rne(float(x)))
+
+
+def philox4x32_10(ctr, key):
+    """Philox-4x32-10 (Salmon et al., SC'11).  ctr: 4 words, key: 2 words."""
+    c = np.array(ctr, dtype=np.uint32)
+    k = np.array(key, dtype=np.uint32)
+    o = np.zeros(4, dtype=np.uint32)
+    lib().orc_philox4x32_10(_ptr(c), _ptr(k), _ptr(o))
+    return [int(v) for v in o]
+
+
+def sr_r16(seed: int, q: int) -> int:
+    return int(lib().orc_sr_r16(seed, q))
+
+
+def sr_r16_fill(seed: int, q0: int, n: int) -> np.ndarray:
+    out = np.zeros(n, dtype=np.uint16)
+    lib().orc_sr_r16_fill(seed, q0, n, _ptr(out))
+    return out
+
+
+def sr_round(x: float, r16: int) -> int:
+    """Stochastic rounding of one fp32 value to bf16 with a given 16-bit
+    random number ("Zero 2 #593", review of vector_add)."""
+    return int(lib().orc_sr_round(float(x), r16))
+
+
+def sr_accumulate(dst: np.ndarray, src: np.ndarray, seed: int, counter_base: int,
+                  zero_src: bool = False):
+    """bf16 dst += src with stochastic rounding (in place on dst; src cleared
+    when zero_src).  Both uint16 bf16 bit arrays of equal size."""
+    assert dst.dtype == np.uint16 and src.dtype == np.uint16 and dst.size == src.size
+    assert dst.flags["C_CONTIGUOUS"] and src.flags["C_CONTIGUOUS"]
+    lib().orc_sr_accumulate(_ptr(dst), _ptr(src), dst.size, seed, counter_base,
+                            1 if zero_src else 0)
+
+
+def volume_bytes(M: int, block_w: int, block_g: int):
+    """Per-step bytes (ZeRO-3, ZeRO++) for M parameters ([ZeRO++] notes,
+    abstract and section 1.2)."""
+    o = np.zeros(2, dtype=np.uint64)
+    lib().orc_volume_bytes(M, block_w, block_g, _ptr(o))
+    return int(o[0]), int(o[1])
