@@ -1,0 +1,187 @@
+/*
+ * zq.h -- C ABI of libzq: the data-parallel hot path of ZeRO++ quantized
+ * communication with LoCo error feedback, and llm.c-style stochastic-rounding
+ * gradient accumulation, as hand-written HIP kernels for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Sources (web pages; each entry point cites the passage that defines it):
+ *   [LoCo]   "Merge LoCo with Zero++" (DeepSpeed pull request 6730):
+ *            Overview; review thread on the per-parameter error-feedback
+ *            buffer and on the LoCo quant kernel.
+ *   [ZeRO++] "ZeROPlusPlus.md" reading notes on the ZeRO++ paper: abstract
+ *            and section 1.2 (qwZ block int8 weights, hpZ, qgZ block int4
+ *            gradients via all-to-all, reduce in full precision, intra-node
+ *            then inter-node).
+ *   [llm.c]  "Zero 2 #593" (llm.c pull request): review of llmc/zero.cuh
+ *            (per-tensor vector_add on the reduced shard, then zeroing) and of
+ *            llmc/cuda_utils.cuh (vector_add with stochastic rounding).
+ *
+ * Conventions shared by every compute entry point
+ *   - Buffers are DEVICE pointers on the current HIP device unless stated.
+ *     The caller allocates and frees everything; libzq never allocates,
+ *     frees, or keeps a pointer past the call, and holds no mutable global
+ *     state, so calls are reentrant and thread-safe.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *     Every call only enqueues kernels on it and returns; results are ready
+ *     when the stream reaches that point.
+ *   - Arguments are validated on the host first; on any error the call
+ *     returns that status and enqueues nothing.  dtype, block and P are
+ *     checked first; then n == 0 is a no-op (ZQ_OK) that touches no pointer.
+ *   - Data streams (g, ef, out, int4/int8 codes, w, dst, src) must be
+ *     16-byte aligned (ZQ_ERR_ALIGN); per-block scale arrays must be 4-byte
+ *     aligned.  Element counts may be any size up to 2^60 (ZQ_ERR_SIZE
+ *     beyond); indexing is 64-bit.
+ *   - block is a power of two in [32, 4096] (ZQ_ERR_BLOCK).
+ *   - Inputs are expected finite.  A NaN or infinity inside a block makes
+ *     that block's scale non-finite; results for it are defined by the same
+ *     arithmetic but are outside the supported contract.
+ *   - Arithmetic is IEEE binary32, round to nearest even, no fused
+ *     multiply-add, denormals kept; integer codes, scales (as bits), error-
+ *     feedback buffers and bf16 outputs are bit-exact functions of the inputs.
+ *
+ * Layouts
+ *   int4 codes: two's-complement nibbles, element 2j in the low nibble of
+ *     byte j; ceil(n/2) bytes; for odd n the last high nibble is 0.
+ *   int8 codes: one int8 per element.
+ *   scales: one fp32 per block of `block` consecutive elements,
+ *     ceil(n/block) of them; a partial last block's scale covers only its
+ *     own elements.
+ *   bf16: uint16 bit patterns.
+ */
+#ifndef ZQ_H
+#define ZQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZQ_ABI_VERSION 1u
+
+typedef enum {
+    ZQ_OK = 0,
+    ZQ_ERR_NULL = 1,   /* a required pointer is NULL                      */
+    ZQ_ERR_SIZE = 2,   /* sizes inconsistent or too large                 */
+    ZQ_ERR_BLOCK = 3,  /* block not a power of two in [32, 4096]          */
+    ZQ_ERR_ALIGN = 4,  /* pointer misaligned (see conventions)            */
+    ZQ_ERR_ALIAS = 5,  /* an output overlaps an input or another output   */
+    ZQ_ERR_PEERS = 6,  /* P outside [1, 16]                               */
+    ZQ_ERR_DTYPE = 7,  /* unknown dtype                                   */
+    ZQ_ERR_LAUNCH = 8  /* the HIP kernel launch itself failed             */
+} zq_status;
+
+typedef enum { ZQ_FP32 = 0, ZQ_BF16 = 1 } zq_dtype;
+
+/*
+ * zq_quantize_ef_int4 -- block int4 gradient quantization with LoCo error
+ * feedback ([LoCo] Overview: error feedback applied to the 4-bit gradients
+ * before communication; [LoCo] review thread: the EF buffer lives with each
+ * parameter; [ZeRO++] section 1.2: qgZ block-based int4 quantization).
+ *
+ * For each block of `block` elements, with e the EF buffer:
+ *   c_i  = fl(g_i + e_i)                 (c_i = g_i when ef == NULL)
+ *   a    = max_i |c_i|,  s = fl(a / 7)
+ *   k_i  = 0 if s == 0, else clamp(round_half_even(fl(c_i / s)), -7, 7)
+ *   d_i  = fl(k_i * s),  r_i = fl(c_i - d_i)
+ *   e_i <- fl(fl(beta_e * e_i) + fl(beta_r * r_i))       (ef != NULL only)
+ * LoCo's literal update is beta_e = beta, beta_r = 1; plain error feedback is
+ * (0, 1); a moving-average reading is (beta, 1 - beta).
+ *
+ *   g       [n] fp32 or bf16 (g_dtype), read only.
+ *   ef      [n] fp32, read-modify-write in place; NULL for no error feedback.
+ *   codes   [ceil(n/2)] bytes, written.     scales [ceil(n/block)] fp32, written.
+ * Errors: NULL g/codes/scales; bad dtype or block; misalignment; codes or
+ * scales overlapping g, ef or each other; ef overlapping g.
+ */
+zq_status zq_quantize_ef_int4(const void *g, zq_dtype g_dtype, float *ef, size_t n,
+                              uint32_t block, float beta_e, float beta_r, uint8_t *codes,
+                              float *scales, void *stream);
+
+/*
+ * zq_dequant_reduce -- qgZ receive side: dequantize the P int4 chunks an
+ * all-to-all delivers to this GPU and reduce them in full precision, with an
+ * optional requantization for the next level of the hierarchy ([ZeRO++]
+ * section 1.2: int4 on the wire, reduction back in full precision, first
+ * inside the node and then across nodes; the kernels are fused to cut
+ * latency).
+ *
+ * For element i of the chunk (block b = i / block):
+ *   S_i = d_{0,i};  S_i = fl(S_i + d_{p,i}) for p = 1 .. P-1,
+ *   d_{p,i} = fl(k_{p,i} * s_{p,b});   R_i = fl(alpha * S_i)
+ * out_i = R_i when out != NULL.  When rq_codes != NULL, R is quantized again
+ * exactly as zq_quantize_ef_int4 does (same block, input R, EF buffer rq_ef
+ * with coefficients rq_beta_e, rq_beta_r, or no EF when rq_ef == NULL).
+ *
+ *   P        number of chunks, 1 <= P <= 16.
+ *   codes    HOST array of P device pointers, each [ceil(n_chunk/2)] bytes.
+ *   scales   HOST array of P device pointers, each [ceil(n_chunk/block)] fp32.
+ *   out      [n_chunk] fp32 written, or NULL.
+ *   rq_codes [ceil(n_chunk/2)] bytes and rq_scales [ceil(n_chunk/block)] fp32
+ *            written, or both NULL.  rq_ef [n_chunk] fp32 read-modify-write
+ *            or NULL (only with rq_codes).
+ * At least one of out / rq_codes is required (ZQ_ERR_NULL otherwise).
+ * Outputs must not overlap any input chunk or each other (ZQ_ERR_ALIAS).
+ */
+zq_status zq_dequant_reduce(uint32_t P, const uint8_t *const *codes, const float *const *scales,
+                            size_t n_chunk, uint32_t block, float alpha, float *out,
+                            uint8_t *rq_codes, float *rq_scales, float *rq_ef, float rq_beta_e,
+                            float rq_beta_r, void *stream);
+
+/*
+ * zq_quant_int8 -- qwZ: block int8 quantization of the weights before the
+ * forward all-gather ([ZeRO++] section 1.2: fp16 to int8, an independent
+ * quantization per block of parameters for accuracy).
+ *   s = fl(max|w| / 127);  k_i = 0 if s == 0 else clamp(rne(fl(w_i / s)), -127, 127)
+ *   w      [n] fp32 or bf16 (w_dtype), read only.
+ *   codes  [n] int8 written.   scales [ceil(n/block)] fp32 written.
+ */
+zq_status zq_quant_int8(const void *w, zq_dtype w_dtype, size_t n, uint32_t block, int8_t *codes,
+                        float *scales, void *stream);
+
+/*
+ * zq_dequant_int8 -- qwZ receive side: w'_i = fl(k_i * s_b), stored as fp32
+ * or rounded to nearest even bf16 ([ZeRO++] section 1.2).
+ *   codes [n] int8, scales [ceil(n/block)] fp32, read only.
+ *   out   [n] fp32 or bf16 (out_dtype), written; must not overlap the inputs.
+ */
+zq_status zq_dequant_int8(const int8_t *codes, const float *scales, size_t n, uint32_t block,
+                          void *out, zq_dtype out_dtype, void *stream);
+
+/*
+ * zq_sr_accumulate -- llm.c ZeRO-2 gradient accumulation into the bf16 shard
+ * with stochastic rounding ([llm.c] review of llmc/cuda_utils.cuh: the sum of
+ * the two bf16 values is formed in fp32 and rounded stochastically, so
+ * accumulation is correct in expectation; review of llmc/zero.cuh: the
+ * zeroing of the reduced buffer can be folded into the same kernel).
+ *
+ *   x_i   = fl(float(dst_i) + float(src_i))
+ *   q     = counter_base + i
+ *   W     = Philox4x32-10(counter = (lo32(q>>3), hi32(q>>3), 0, 0),
+ *                         key = (lo32(seed), hi32(seed)))
+ *   r16   = 16-bit half (q & 1) (low half first) of word W[(q & 7) >> 1]
+ *   dst_i = 0x7FC0 if x_i is NaN, else ((bits(x_i) + r16) mod 2^32) >> 16
+ *   src_i = 0 afterwards when zero_src != 0.
+ * Using the GLOBAL element index as the counter makes a shard's accumulation
+ * (counter_base = shard offset) bit-identical to the same slice of a
+ * full-buffer accumulation.
+ *
+ *   dst [n] bf16 read-modify-write;  src [n] bf16 read (written when
+ *   zero_src).  dst and src must not overlap (ZQ_ERR_ALIAS).  counter_base + n
+ *   must not exceed 2^64 - 1 (ZQ_ERR_SIZE).
+ */
+zq_status zq_sr_accumulate(uint16_t *dst_bf16, uint16_t *src_bf16, size_t n, uint64_t seed,
+                           uint64_t counter_base, int zero_src, void *stream);
+
+/* Host-only helpers (no device work, usable without a GPU). */
+size_t zq_int4_code_bytes(size_t n);               /* ceil(n/2)                        */
+size_t zq_num_blocks(size_t n, uint32_t block);    /* ceil(n/block); 0 if block == 0   */
+const char *zq_status_str(zq_status s);            /* static string, never NULL        */
+uint32_t zq_abi_version(void);                     /* ZQ_ABI_VERSION                   */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZQ_H */

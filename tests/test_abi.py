@@ -1,0 +1,127 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/zq.h declares, its host helpers agree with the layout rules, and
+every validation error returns its status before any device work (all
+pointers below are fake and never dereferenced).  The host helpers are also
+tied to the pages' communication-volume closed form via the oracle."""
+import ctypes as C
+
+import pytest
+
+import oracle as O
+from weight_communication_zero_amd import zq
+
+L = zq.lib
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def test_exports_every_declared_symbol():
+    names = zq.declared_symbols()
+    assert set(names) == {"zq_quantize_ef_int4", "zq_dequant_reduce", "zq_quant_int8",
+                          "zq_dequant_int8", "zq_sr_accumulate", "zq_int4_code_bytes",
+                          "zq_num_blocks", "zq_status_str", "zq_abi_version"}
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_host_helpers():
+    assert L.zq_abi_version() == 1
+    for n in [0, 1, 2, 3, 4095, 2 ** 33 + 1]:
+        assert L.zq_int4_code_bytes(n) == (n + 1) // 2
+        for b in [32, 128, 4096]:
+            assert L.zq_num_blocks(n, b) == -(-n // b)
+    assert L.zq_num_blocks(10, 0) == 0
+    for s in range(9):
+        assert L.zq_status_str(s).decode().startswith(zq.STATUS[s])
+    assert L.zq_status_str(99).decode() == "unknown zq_status"
+
+
+def test_volume_from_library_buffer_sizes_matches_pages():
+    """Bytes libzq's layout puts on the wire (codes + fp32 scales) for the
+    0.85B model at the int8 / int4 block sizes equal the oracle's closed form
+    of the pages' 0.5M + 0 + 0.25M count."""
+    M = 850454528
+    int8_bytes = M + 4 * L.zq_num_blocks(M, 2048)
+    int4_bytes = L.zq_int4_code_bytes(M) + 4 * L.zq_num_blocks(M, 128)
+    zero3, zpp = O.volume_bytes(M, 2048, 128)
+    assert int8_bytes + 0 + int4_bytes == zpp and zero3 == 6 * M
+
+
+def efq(g=FAKE, dt=0, ef=None, n=1024, block=128, codes=FAKE + 0x100000, scales=FAKE + 0x200000):
+    return L.zq_quantize_ef_int4(g, dt, ef, n, block, 1.0, 1.0, codes, scales, None)
+
+
+def test_quantize_validation():
+    assert efq(dt=2) == zq.ZQ_ERR_DTYPE
+    for b in [0, 16, 100, 8192, 129]:
+        assert efq(block=b) == zq.ZQ_ERR_BLOCK
+    assert efq(n=(1 << 60) + 1) == zq.ZQ_ERR_SIZE
+    assert efq(g=None, n=0) == zq.ZQ_OK  # n == 0 touches no pointer
+    assert efq(g=None) == zq.ZQ_ERR_NULL
+    assert efq(codes=None) == zq.ZQ_ERR_NULL
+    assert efq(scales=None) == zq.ZQ_ERR_NULL
+    assert efq(g=FAKE + 4) == zq.ZQ_ERR_ALIGN
+    assert efq(ef=FAKE + 0x300008) == zq.ZQ_ERR_ALIGN
+    assert efq(codes=FAKE + 0x100001) == zq.ZQ_ERR_ALIGN
+    assert efq(scales=FAKE + 0x200002) == zq.ZQ_ERR_ALIGN
+    assert efq(codes=FAKE + 0x10) == zq.ZQ_ERR_ALIAS  # codes inside g
+    assert efq(scales=FAKE + 0x100010) == zq.ZQ_ERR_ALIAS  # scales inside codes
+    assert efq(ef=FAKE + 0x10) == zq.ZQ_ERR_ALIAS  # ef overlaps g
+    assert efq(ef=FAKE + 0x300000, codes=FAKE + 0x300000) == zq.ZQ_ERR_ALIAS
+
+
+def dr(P=4, codes=None, scales=None, n=1024, block=128, out=FAKE + 0x400000, rq_codes=None,
+       rq_scales=None, rq_ef=None):
+    cp = codes or [FAKE + 0x1000 * i for i in range(max(P, 1))]
+    sp = scales or [FAKE + 0x100000 + 0x1000 * i for i in range(max(P, 1))]
+    ca = (C.c_void_p * len(cp))(*cp)
+    sa = (C.c_void_p * len(sp))(*sp)
+    return L.zq_dequant_reduce(P, ca, sa, n, block, 0.25, out, rq_codes, rq_scales, rq_ef, 0.0, 1.0,
+                               None)
+
+
+def test_dequant_reduce_validation():
+    assert dr(P=0) == zq.ZQ_ERR_PEERS
+    assert dr(P=17) == zq.ZQ_ERR_PEERS
+    assert dr(block=48) == zq.ZQ_ERR_BLOCK
+    assert dr(n=0, out=None) == zq.ZQ_OK
+    assert dr(out=None) == zq.ZQ_ERR_NULL  # neither out nor requant
+    assert dr(codes=[FAKE, None, FAKE + 0x2000, FAKE + 0x3000]) == zq.ZQ_ERR_NULL
+    assert dr(rq_codes=FAKE + 0x500000) == zq.ZQ_ERR_NULL  # rq_scales missing
+    assert dr(rq_ef=FAKE + 0x600000) == zq.ZQ_ERR_NULL  # rq_ef without requant
+    assert dr(codes=[FAKE + 8, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000]) == zq.ZQ_ERR_ALIGN
+    assert dr(out=FAKE + 0x400004) == zq.ZQ_ERR_ALIGN
+    assert dr(out=FAKE + 0x1000) == zq.ZQ_ERR_ALIAS  # out over chunk 1's codes
+    assert dr(rq_codes=FAKE + 0x400100, rq_scales=FAKE + 0x500000) == zq.ZQ_ERR_ALIAS
+    assert dr(out=None, rq_codes=FAKE + 0x500000, rq_scales=FAKE + 0x100000) == zq.ZQ_ERR_ALIAS
+
+
+def test_int8_and_sr_validation():
+    q8 = lambda **k: L.zq_quant_int8(k.get("w", FAKE), k.get("dt", 1), k.get("n", 4096),
+                                     k.get("block", 2048), k.get("codes", FAKE + 0x100000),
+                                     k.get("scales", FAKE + 0x200000), None)
+    assert q8(dt=5) == zq.ZQ_ERR_DTYPE
+    assert q8(block=3000) == zq.ZQ_ERR_BLOCK
+    assert q8(w=None) == zq.ZQ_ERR_NULL
+    assert q8(codes=FAKE + 0x100008) == zq.ZQ_ERR_ALIGN
+    assert q8(codes=FAKE + 0x1000) == zq.ZQ_ERR_ALIAS
+    dq = lambda **k: L.zq_dequant_int8(k.get("codes", FAKE), k.get("scales", FAKE + 0x100000),
+                                       k.get("n", 4096), 2048, k.get("out", FAKE + 0x200000),
+                                       k.get("dt", 1), None)
+    assert dq(dt=9) == zq.ZQ_ERR_DTYPE
+    assert dq(out=None) == zq.ZQ_ERR_NULL
+    assert dq(out=FAKE + 0x200002) == zq.ZQ_ERR_ALIGN
+    assert dq(out=FAKE + 0x800) == zq.ZQ_ERR_ALIAS
+    sr = lambda **k: L.zq_sr_accumulate(k.get("dst", FAKE), k.get("src", FAKE + 0x100000),
+                                        k.get("n", 4096), 1, k.get("cb", 0), 0, None)
+    assert sr(n=0, dst=None) == zq.ZQ_OK
+    assert sr(dst=None) == zq.ZQ_ERR_NULL
+    assert sr(src=FAKE + 0x100004) == zq.ZQ_ERR_ALIGN
+    assert sr(src=FAKE + 0x1000) == zq.ZQ_ERR_ALIAS
+    assert sr(cb=(1 << 64) - 100) == zq.ZQ_ERR_SIZE
+
+
+def test_binding_guards_reject_short_or_host_buffers():
+    import torch
+    with pytest.raises(ValueError):
+        zq.zq_quantize_ef_int4(torch.zeros(16), None, 32, 1.0, 1.0, torch.zeros(8, dtype=torch.uint8),
+                               torch.zeros(1))

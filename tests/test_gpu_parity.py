@@ -1,0 +1,314 @@
+"""GPU parity: libzq's HIP kernels (through the C ABI) against the CPU oracle,
+element by element on the same seeded inputs, at sizes that span several
+wave tiles and a ragged tail, for every block size and input dtype, with the
+edge cases of the method (zero / signed-zero / subnormal / tie / huge blocks,
+odd n, n = 1, P = 1 and P = 16, every Philox counter phase, NaN / Inf in
+stochastic rounding).  Contract: integer codes, scales (as bits), EF buffers,
+requant codes and bf16 outputs bit-exact; fp32 reduced sums within 1e-6
+relative of the oracle (guarded by the sum of magnitudes) -- and, as the op
+order is fixed, expected bit-exact too.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from tests.gpu_helpers import (Guarded, as_bf16_bits, assert_bits_equal, bf16_to_f32,
+                               grad_values, to_gpu, to_host)
+
+pytestmark = pytest.mark.gpu
+
+BLOCKS = [32, 64, 128, 256, 512, 1024, 2048, 4096]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import weight_communication_zero_amd  # noqa: F401  (fails loudly if libzq.so is missing)
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def Z():
+    from weight_communication_zero_amd import zq
+    return zq
+
+
+def sizes_for(block, vec_tile):
+    tile = max(vec_tile, block)
+    return [1, 3, block - 1, block + 1, tile + 5, 3 * tile + block // 2 + 3, 5 * tile]
+
+
+# ------------------------------------------------------- EF int4 quantize --
+
+def run_efq_gpu(g_host, ef_host, block, be, br):
+    n = g_host.size
+    g = to_gpu(g_host)
+    ef = to_gpu(ef_host) if ef_host is not None else None
+    codes = Guarded((n + 1) // 2, torch.uint8)
+    scales = Guarded(-(-n // block), torch.float32)
+    Z().zq_quantize_ef_int4(g, ef, block, be, br, codes.t, scales.t)
+    torch.cuda.synchronize()
+    return codes.host(), scales.host(), (to_host(ef) if ef is not None else None)
+
+
+def check_efq(g_host, ef_host, block, be, br, what):
+    ef_o = ef_host.copy() if ef_host is not None else None
+    c_o, s_o = O.quantize_ef_int4(g_host, ef_o, block, be, br)
+    c_g, s_g, ef_g = run_efq_gpu(g_host, ef_host.copy() if ef_host is not None else None, block,
+                                 be, br)
+    assert_bits_equal(c_g, c_o, f"{what} codes")
+    assert_bits_equal(s_g, s_o, f"{what} scales")
+    if ef_host is not None:
+        assert_bits_equal(ef_g, ef_o, f"{what} ef")
+
+
+@pytest.mark.parametrize("block", BLOCKS)
+@pytest.mark.parametrize("gdt", ["fp32", "bf16"])
+@pytest.mark.parametrize("with_ef", [False, True])
+def test_efq_matches_oracle(block, gdt, with_ef):
+    for i, n in enumerate(sizes_for(block, 1024)):
+        x = grad_values(n, seed=1000 * block + i, special=True, block=block)
+        g = as_bf16_bits(x) if gdt == "bf16" else x
+        ef = (grad_values(n, seed=7 + i, std=1e-5) if with_ef else None)
+        check_efq(g, ef, block, 0.9, 1.0, f"efq n={n} B={block} {gdt} ef={with_ef}")
+
+
+@pytest.mark.parametrize("betas", [(1.0, 1.0), (0.0, 1.0), (0.9, 0.1), (0.0, 0.9)])
+def test_efq_beta_variants_multistep(betas):
+    n, block = 3 * 4096 + 77, 128
+    ef_o = np.zeros(n, np.float32)
+    ef_g = torch.zeros(n, dtype=torch.float32, device="cuda")
+    for step in range(3):
+        g = grad_values(n, seed=50 + step, special=(step == 1))
+        c_o, s_o = O.quantize_ef_int4(g, ef_o, block, *betas)
+        codes = Guarded((n + 1) // 2, torch.uint8)
+        scales = Guarded(-(-n // block), torch.float32)
+        Z().zq_quantize_ef_int4(to_gpu(g), ef_g, block, betas[0], betas[1], codes.t, scales.t)
+        torch.cuda.synchronize()
+        assert_bits_equal(codes.host(), c_o, f"codes step {step}")
+        assert_bits_equal(scales.host(), s_o, f"scales step {step}")
+        assert_bits_equal(to_host(ef_g), ef_o, f"ef step {step}")
+
+
+def test_efq_random_ties_band():
+    """Values that sit exactly on, and within an ulp or two of, the rounding
+    boundaries k + 1/2 of their block -- the inputs where the kernel's
+    reciprocal fast path must hand over to the IEEE quotient."""
+    rng = np.random.default_rng(3)
+    block, nb = 128, 512
+    out = []
+    for b in range(nb):
+        s = np.float32(2.0 ** rng.integers(-30, 30) * rng.uniform(1, 2))
+        ks = rng.integers(-7, 7, size=block) + 0.5
+        x = (ks * s).astype(np.float32)
+        d = rng.integers(-1, 2, size=block)
+        target = np.where(d < 0, -np.inf, np.where(d > 0, np.inf, x)).astype(np.float32)
+        x = np.nextafter(x, target)
+        x[0] = np.float32(7) * s  # absmax 7s: scale s (or its rounding)
+        out.append(x.astype(np.float32))
+    g = np.concatenate(out)
+    check_efq(g, None, block, 0.0, 1.0, "tie band int4")
+    check_efq(g, np.zeros_like(g), block, 0.0, 1.0, "tie band int4 with ef")
+
+
+def test_efq_n_zero_is_noop():
+    zq = Z()
+    codes = torch.full((4,), 0xAA, dtype=torch.uint8, device="cuda")
+    zq.zq_quantize_ef_int4(torch.zeros(0, device="cuda"), None, 128, 1.0, 1.0, codes,
+                           torch.zeros(1, device="cuda"))
+    torch.cuda.synchronize()
+    assert (codes.cpu() == 0xAA).all()
+
+
+def test_error_enqueues_nothing():
+    zq = Z()
+    n = 4096
+    codes = torch.full((n // 2,), 0xAA, dtype=torch.uint8, device="cuda")
+    scales = torch.full((n // 128,), 7.0, device="cuda")
+    g = torch.ones(n, device="cuda")
+    st = zq.lib.zq_quantize_ef_int4(g.data_ptr(), 0, None, n, 100, 1.0, 1.0, codes.data_ptr(),
+                                    scales.data_ptr(), None)
+    assert st == zq.ZQ_ERR_BLOCK
+    st = zq.lib.zq_quantize_ef_int4(g.data_ptr(), 0, g.data_ptr(), n, 128, 1.0, 1.0,
+                                    codes.data_ptr(), scales.data_ptr(), None)
+    assert st == zq.ZQ_ERR_ALIAS
+    torch.cuda.synchronize()
+    assert (codes.cpu() == 0xAA).all() and (scales.cpu() == 7.0).all()
+
+
+# ---------------------------------------------------- dequantize + reduce --
+
+def make_chunks(P, n, block, seed, raw=False):
+    """P int4 chunks: quantized random gradients (as a sender would make
+    them), or raw random nibbles (-8 included) with random scales."""
+    rng = np.random.default_rng(seed)
+    codes, scales = [], []
+    for p in range(P):
+        if raw:
+            c = rng.integers(0, 256, size=(n + 1) // 2, dtype=np.uint8)
+            if n % 2:
+                c[-1] &= 0x0F
+            s = (rng.standard_normal(-(-n // block)) * 1e-4).astype(np.float32)
+            s[rng.random(s.size) < 0.05] = 0.0
+            s[rng.random(s.size) < 0.02] = np.float32(1e-41)
+        else:
+            x = grad_values(n, seed=seed * 31 + p, std=10.0 ** rng.uniform(-5, -2),
+                            special=True, block=block)
+            c, s = O.quantize_ef_int4(x, None, block, 0.0, 1.0)
+        codes.append(c)
+        scales.append(s)
+    return codes, scales
+
+
+def check_dr(P, n, block, alpha, want_out, requant, with_rq_ef, seed, raw=False):
+    codes, scales = make_chunks(P, n, block, seed, raw=raw)
+    rq_ef_host = grad_values(n, seed=seed + 99, std=1e-6) if with_rq_ef else None
+    rq_ef_o = rq_ef_host.copy() if with_rq_ef else None
+    out_o, rqc_o, rqs_o = O.dequant_reduce(codes, scales, n, block, alpha, want_out=want_out,
+                                           requant=requant, rq_ef=rq_ef_o, rq_beta_e=0.9,
+                                           rq_beta_r=1.0)
+    cg = [to_gpu(c) for c in codes]
+    sg = [to_gpu(s) for s in scales]
+    out = Guarded(n, torch.float32) if want_out else None
+    rqc = Guarded((n + 1) // 2, torch.uint8) if requant else None
+    rqs = Guarded(-(-n // block), torch.float32) if requant else None
+    rq_ef = to_gpu(rq_ef_host) if with_rq_ef else None
+    Z().zq_dequant_reduce(cg, sg, n, block, alpha, out=out.t if out else None,
+                          rq_codes=rqc.t if rqc else None, rq_scales=rqs.t if rqs else None,
+                          rq_ef=rq_ef, rq_beta_e=0.9, rq_beta_r=1.0)
+    torch.cuda.synchronize()
+    what = f"dr P={P} n={n} B={block} a={alpha} out={want_out} rq={requant} rqef={with_rq_ef}"
+    if want_out:
+        got = out.host()
+        # contract: 1e-6 relative, guarded by the sum of |d_p|
+        mag = np.zeros(n, np.float64)
+        for c, s in zip(codes, scales):
+            k = np.empty(2 * c.size, np.int16)
+            k[0::2], k[1::2] = c & 0x0F, c >> 4
+            k = np.where(k >= 8, k - 16, k)[:n]
+            mag += np.abs(k.astype(np.float64) * np.repeat(s.astype(np.float64), block)[:n])
+        tol = 1e-6 * np.maximum(np.abs(out_o.astype(np.float64)), abs(alpha) * mag)
+        assert (np.abs(got.astype(np.float64) - out_o) <= tol).all(), what
+        assert_bits_equal(got, out_o, what + " out")
+    if requant:
+        assert_bits_equal(rqc.host(), rqc_o, what + " rq_codes")
+        assert_bits_equal(rqs.host(), rqs_o, what + " rq_scales")
+    if with_rq_ef:
+        assert_bits_equal(to_host(rq_ef), rq_ef_o, what + " rq_ef")
+
+
+@pytest.mark.parametrize("block", BLOCKS)
+@pytest.mark.parametrize("P", [1, 2, 3, 4, 8, 13, 16])
+def test_dequant_reduce_out(block, P):
+    for i, n in enumerate([block, max(1024, block) * 3 + block // 2 + 1, max(1024, block) * 4]):
+        check_dr(P, n, block, 1.0 / 8 if P > 1 else 1.0, True, False, False, seed=block * P + i)
+
+
+@pytest.mark.parametrize("block", BLOCKS)
+@pytest.mark.parametrize("flags", [(True, True, False), (False, True, False), (False, True, True),
+                                   (True, True, True)])
+def test_dequant_reduce_requant(block, flags):
+    want_out, requant, rqef = flags
+    for i, (P, n) in enumerate([(8, max(1024, block) * 3 + 17), (4, max(1024, block) * 2),
+                                (1, 2 * block - 1)]):
+        check_dr(P, n, block, 1.0, want_out, requant, rqef, seed=7 * block + i)
+
+
+@pytest.mark.parametrize("alpha", [1.0, 0.25, 1.0 / 3.0, -2.0])
+def test_dequant_reduce_alpha_and_raw_codes(alpha):
+    check_dr(6, 4096 * 3 + 5, 128, alpha, True, True, True, seed=11, raw=True)
+    check_dr(16, 2048 + 1, 64, alpha, True, True, False, seed=12, raw=True)
+
+
+# ---------------------------------------------------------------- qwZ int8 --
+
+@pytest.mark.parametrize("block", BLOCKS)
+@pytest.mark.parametrize("wdt", ["fp32", "bf16"])
+def test_quant_dequant_int8(block, wdt):
+    for i, n in enumerate(sizes_for(block, 1024)):
+        x = grad_values(n, seed=300 * block + i, std=0.02, special=True, block=block)
+        w = as_bf16_bits(x) if wdt == "bf16" else x
+        c_o, s_o = O.quant_int8(w, block)
+        codes = Guarded(n, torch.int8)
+        scales = Guarded(-(-n // block), torch.float32)
+        Z().zq_quant_int8(to_gpu(w), block, codes.t, scales.t)
+        torch.cuda.synchronize()
+        what = f"q8 n={n} B={block} {wdt}"
+        c_g, s_g = codes.host(), scales.host()
+        assert_bits_equal(c_g.view(np.uint8), c_o.view(np.uint8), what + " codes")
+        assert_bits_equal(s_g, s_o, what + " scales")
+        for out_bf16 in (True, False):
+            o_o = O.dequant_int8(c_o, s_o, block, out_bf16=out_bf16)
+            out = Guarded(n, torch.bfloat16 if out_bf16 else torch.float32)
+            Z().zq_dequant_int8(to_gpu(c_o), to_gpu(s_o), block, out.t)
+            torch.cuda.synchronize()
+            assert_bits_equal(out.host(), o_o, what + f" dequant bf16={out_bf16}")
+
+
+# ------------------------------------------------------ stochastic rounding --
+
+def sr_inputs(n, seed, special=False):
+    rng = np.random.default_rng(seed)
+    d = as_bf16_bits((rng.standard_normal(n) * 1e-2).astype(np.float32))
+    s = as_bf16_bits((rng.standard_normal(n) * 1e-4).astype(np.float32))
+    if special and n >= 16:
+        idx = rng.choice(n, size=min(n, 16), replace=False)
+        d[idx[0]] = 0x7FC0  # NaN
+        d[idx[1]] = 0x7F80  # +inf
+        d[idx[2]] = 0xFF80  # -inf
+        d[idx[3]] = 0x7F7F  # near max: may round up to inf
+        s[idx[3]] = 0x7B00
+        d[idx[4]] = 0x8000  # -0
+        s[idx[4]] = 0x8000
+        d[idx[5]] = 0x0001  # subnormal
+        s[idx[5]] = 0x0001
+        d[idx[6]] = 0x3F80
+        s[idx[6]] = 0x3B80
+    return d, s
+
+
+@pytest.mark.parametrize("phase", range(8))
+@pytest.mark.parametrize("zero_src", [False, True])
+def test_sr_matches_oracle(phase, zero_src):
+    for i, n in enumerate([1, 7, 8, 1023, 1024, 1024 * 5 + 9, 1 << 17]):
+        d, s = sr_inputs(n, seed=10 * phase + i, special=True)
+        seed = 0x1234_5678_9ABC_DEF0 + i
+        cb = 8 * (3 + 1000 * i) + phase
+        d_o, s_o = d.copy(), s.copy()
+        O.sr_accumulate(d_o, s_o, seed, cb, zero_src)
+        dg, sg = to_gpu(d), to_gpu(s)
+        Z().zq_sr_accumulate(dg, sg, seed, cb, zero_src)
+        torch.cuda.synchronize()
+        what = f"sr n={n} phase={phase} zero={zero_src}"
+        assert_bits_equal(to_host(dg), d_o, what + " dst")
+        assert_bits_equal(to_host(sg), s_o, what + " src")
+
+
+def test_sr_counter_above_2_pow_35():
+    """Counters whose Philox counter needs its high word."""
+    n = 4096 + 3
+    d, s = sr_inputs(n, seed=5)
+    cb = (1 << 35) * 8 + 5
+    d_o = d.copy()
+    O.sr_accumulate(d_o, s.copy(), 42, cb, False)
+    dg = to_gpu(d)
+    Z().zq_sr_accumulate(dg, to_gpu(s), 42, cb)
+    torch.cuda.synchronize()
+    assert_bits_equal(to_host(dg), d_o, "sr high counter")
+
+
+def test_sr_shard_equals_slice_of_full_run_on_gpu():
+    n, P, rank = 8 * 40000, 8, 3
+    shard = n // P
+    off = rank * shard
+    full = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    part = torch.zeros(shard, dtype=torch.bfloat16, device="cuda")
+    for m in range(8):
+        src = torch.randn(n, generator=torch.Generator().manual_seed(m)).mul_(1e-4).to(torch.bfloat16).cuda()
+        Z().zq_sr_accumulate(full, src, m, 0)
+        Z().zq_sr_accumulate(part, src[off:off + shard].contiguous(), m, off)
+    torch.cuda.synchronize()
+    assert torch.equal(full[off:off + shard].view(torch.int16), part.view(torch.int16))

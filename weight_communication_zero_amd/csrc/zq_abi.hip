@@ -1,0 +1,194 @@
+// zq_abi.hip -- the extern "C" entry points of libzq: host-side argument
+// validation, then one kernel launch on the caller's stream.  Every check
+// runs before anything is enqueued, so an error status means no device work
+// was issued.  No state, no allocation.
+#include <stdint.h>
+
+#include "../../include/zq.h"
+#include "zq_launch.h"
+
+namespace {
+
+constexpr size_t kMaxElems = (size_t)1 << 60;
+
+bool valid_block(uint32_t b) { return b >= 32 && b <= 4096 && (b & (b - 1)) == 0; }
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Byte ranges [a, a+na) and [b, b+nb) intersect (NULL or empty never does).
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0)
+        return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+size_t nblocks(size_t n, uint32_t block) { return (n + block - 1) / block; }
+
+zq_status launched(hipError_t e) { return e == hipSuccess ? ZQ_OK : ZQ_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+zq_status zq_quantize_ef_int4(const void* g, zq_dtype g_dtype, float* ef, size_t n, uint32_t block,
+                              float beta_e, float beta_r, uint8_t* codes, float* scales,
+                              void* stream) {
+    if (g_dtype != ZQ_FP32 && g_dtype != ZQ_BF16)
+        return ZQ_ERR_DTYPE;
+    if (!valid_block(block))
+        return ZQ_ERR_BLOCK;
+    if (n > kMaxElems)
+        return ZQ_ERR_SIZE;
+    if (n == 0)
+        return ZQ_OK;
+    if (!g || !codes || !scales)
+        return ZQ_ERR_NULL;
+    if (!aligned(g, 16) || !aligned(ef, 16) || !aligned(codes, 16) || !aligned(scales, 4))
+        return ZQ_ERR_ALIGN;
+    const size_t gb = n * (g_dtype == ZQ_BF16 ? 2 : 4), eb = ef ? n * 4 : 0;
+    const size_t cb = zq_int4_code_bytes(n), sb = nblocks(n, block) * 4;
+    if (overlap(codes, cb, g, gb) || overlap(codes, cb, ef, eb) || overlap(codes, cb, scales, sb) ||
+        overlap(scales, sb, g, gb) || overlap(scales, sb, ef, eb) || overlap(ef, eb, g, gb))
+        return ZQ_ERR_ALIAS;
+    return launched(zq::launch_quantize_ef_int4(g, g_dtype == ZQ_BF16, ef, n, block, beta_e,
+                                                beta_r, codes, scales, (hipStream_t)stream));
+}
+
+zq_status zq_dequant_reduce(uint32_t P, const uint8_t* const* codes, const float* const* scales,
+                            size_t n_chunk, uint32_t block, float alpha, float* out,
+                            uint8_t* rq_codes, float* rq_scales, float* rq_ef, float rq_beta_e,
+                            float rq_beta_r, void* stream) {
+    if (P < 1 || P > zq::kMaxPeers)
+        return ZQ_ERR_PEERS;
+    if (!valid_block(block))
+        return ZQ_ERR_BLOCK;
+    if (n_chunk > kMaxElems)
+        return ZQ_ERR_SIZE;
+    if (n_chunk == 0)
+        return ZQ_OK;
+    if (!codes || !scales)
+        return ZQ_ERR_NULL;
+    for (uint32_t p = 0; p < P; ++p)
+        if (!codes[p] || !scales[p])
+            return ZQ_ERR_NULL;
+    if (!out && !rq_codes)
+        return ZQ_ERR_NULL;
+    if ((rq_codes == nullptr) != (rq_scales == nullptr) || (rq_ef && !rq_codes))
+        return ZQ_ERR_NULL;
+    for (uint32_t p = 0; p < P; ++p)
+        if (!aligned(codes[p], 16) || !aligned(scales[p], 4))
+            return ZQ_ERR_ALIGN;
+    if (!aligned(out, 16) || !aligned(rq_codes, 16) || !aligned(rq_scales, 4) ||
+        !aligned(rq_ef, 16))
+        return ZQ_ERR_ALIGN;
+    const size_t cb = zq_int4_code_bytes(n_chunk), sb = nblocks(n_chunk, block) * 4;
+    const size_t ob = out ? n_chunk * 4 : 0, rcb = rq_codes ? cb : 0, rsb = rq_codes ? sb : 0;
+    const size_t reb = rq_ef ? n_chunk * 4 : 0;
+    const void* outs[4] = {out, rq_codes, rq_scales, rq_ef};
+    const size_t outb[4] = {ob, rcb, rsb, reb};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outb[i], outs[j], outb[j]))
+                return ZQ_ERR_ALIAS;
+        for (uint32_t p = 0; p < P; ++p)
+            if (overlap(outs[i], outb[i], codes[p], cb) || overlap(outs[i], outb[i], scales[p], sb))
+                return ZQ_ERR_ALIAS;
+    }
+    zq::DrParams prm = {};
+    for (uint32_t p = 0; p < P; ++p) {
+        prm.codes[p] = codes[p];
+        prm.scales[p] = scales[p];
+    }
+    prm.P = P;
+    prm.n = n_chunk;
+    prm.alpha = alpha;
+    prm.out = out;
+    prm.rq_codes = rq_codes;
+    prm.rq_scales = rq_scales;
+    prm.rq_ef = rq_ef;
+    prm.rq_beta_e = rq_beta_e;
+    prm.rq_beta_r = rq_beta_r;
+    return launched(zq::launch_dequant_reduce(prm, block, (hipStream_t)stream));
+}
+
+zq_status zq_quant_int8(const void* w, zq_dtype w_dtype, size_t n, uint32_t block, int8_t* codes,
+                        float* scales, void* stream) {
+    if (w_dtype != ZQ_FP32 && w_dtype != ZQ_BF16)
+        return ZQ_ERR_DTYPE;
+    if (!valid_block(block))
+        return ZQ_ERR_BLOCK;
+    if (n > kMaxElems)
+        return ZQ_ERR_SIZE;
+    if (n == 0)
+        return ZQ_OK;
+    if (!w || !codes || !scales)
+        return ZQ_ERR_NULL;
+    if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scales, 4))
+        return ZQ_ERR_ALIGN;
+    const size_t wb = n * (w_dtype == ZQ_BF16 ? 2 : 4), sb = nblocks(n, block) * 4;
+    if (overlap(codes, n, w, wb) || overlap(scales, sb, w, wb) || overlap(codes, n, scales, sb))
+        return ZQ_ERR_ALIAS;
+    return launched(
+        zq::launch_quant_int8(w, w_dtype == ZQ_BF16, n, block, codes, scales, (hipStream_t)stream));
+}
+
+zq_status zq_dequant_int8(const int8_t* codes, const float* scales, size_t n, uint32_t block,
+                          void* out, zq_dtype out_dtype, void* stream) {
+    if (out_dtype != ZQ_FP32 && out_dtype != ZQ_BF16)
+        return ZQ_ERR_DTYPE;
+    if (!valid_block(block))
+        return ZQ_ERR_BLOCK;
+    if (n > kMaxElems)
+        return ZQ_ERR_SIZE;
+    if (n == 0)
+        return ZQ_OK;
+    if (!codes || !scales || !out)
+        return ZQ_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(scales, 4) || !aligned(out, 16))
+        return ZQ_ERR_ALIGN;
+    const size_t ob = n * (out_dtype == ZQ_BF16 ? 2 : 4), sb = nblocks(n, block) * 4;
+    if (overlap(out, ob, codes, n) || overlap(out, ob, scales, sb))
+        return ZQ_ERR_ALIAS;
+    return launched(zq::launch_dequant_int8(codes, scales, n, block, out, out_dtype == ZQ_BF16,
+                                            (hipStream_t)stream));
+}
+
+zq_status zq_sr_accumulate(uint16_t* dst_bf16, uint16_t* src_bf16, size_t n, uint64_t seed,
+                           uint64_t counter_base, int zero_src, void* stream) {
+    if (n > kMaxElems || counter_base > UINT64_MAX - n)
+        return ZQ_ERR_SIZE;
+    if (n == 0)
+        return ZQ_OK;
+    if (!dst_bf16 || !src_bf16)
+        return ZQ_ERR_NULL;
+    if (!aligned(dst_bf16, 16) || !aligned(src_bf16, 16))
+        return ZQ_ERR_ALIGN;
+    if (overlap(dst_bf16, n * 2, src_bf16, n * 2))
+        return ZQ_ERR_ALIAS;
+    return launched(zq::launch_sr_accumulate(dst_bf16, src_bf16, n, seed, counter_base,
+                                             zero_src != 0, (hipStream_t)stream));
+}
+
+size_t zq_int4_code_bytes(size_t n) { return n / 2 + (n & 1); }
+
+size_t zq_num_blocks(size_t n, uint32_t block) { return block ? nblocks(n, block) : 0; }
+
+const char* zq_status_str(zq_status s) {
+    switch (s) {
+        case ZQ_OK: return "ZQ_OK";
+        case ZQ_ERR_NULL: return "ZQ_ERR_NULL: a required pointer is NULL";
+        case ZQ_ERR_SIZE: return "ZQ_ERR_SIZE: sizes inconsistent or too large";
+        case ZQ_ERR_BLOCK: return "ZQ_ERR_BLOCK: block must be a power of two in [32, 4096]";
+        case ZQ_ERR_ALIGN: return "ZQ_ERR_ALIGN: misaligned pointer";
+        case ZQ_ERR_ALIAS: return "ZQ_ERR_ALIAS: an output overlaps another buffer";
+        case ZQ_ERR_PEERS: return "ZQ_ERR_PEERS: P must be in [1, 16]";
+        case ZQ_ERR_DTYPE: return "ZQ_ERR_DTYPE: unknown dtype";
+        case ZQ_ERR_LAUNCH: return "ZQ_ERR_LAUNCH: HIP kernel launch failed";
+    }
+    return "unknown zq_status";
+}
+
+uint32_t zq_abi_version(void) { return ZQ_ABI_VERSION; }
+
+}  // extern "C"

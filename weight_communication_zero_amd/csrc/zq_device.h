@@ -1,0 +1,188 @@
+// zq_device.h -- device helpers shared by the libzq kernels (gfx950, wave64).
+//
+// Everything here is register-level: 16-byte vector types, DPP / permlane
+// cross-lane maxima, bf16 conversion, the int4/int8 block quantizer step and
+// Philox-4x32-10.  Nothing here allocates or touches LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace zq {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kBlockThreads = 256;  // 4 waves per workgroup
+constexpr int kWavesPerWG = kBlockThreads / kWave;
+
+__device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float bitsf(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// bf16 bit pattern -> fp32 (exact).
+__device__ __forceinline__ float bf16lo(uint32_t w) { return bitsf(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return bitsf(w & 0xFFFF0000u); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+// Only used on finite values.
+__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    bf2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// |x| as an unsigned bit pattern: for non-NaN values its unsigned order is
+// the order of the magnitudes, so a max over these bits is the exact absmax.
+__device__ __forceinline__ uint32_t absbits(float x) { return fbits(x) & 0x7FFFFFFFu; }
+
+// ---------------------------------------------------------------------------
+// Maximum over aligned groups of G consecutive lanes (G a power of two <= 64);
+// every lane of the group receives the group maximum.  Butterfly on DPP:
+// quad_perm swaps (xor 1, xor 2), row half-mirror (pairs quads within 8),
+// row mirror (pairs half-rows within 16), ds_swizzle xor 16 (within 32), and
+// gfx950's v_permlane32_swap (exchanges the two 32-lane halves).
+template <int G>
+__device__ __forceinline__ uint32_t group_max(uint32_t v) {
+    if constexpr (G >= 2)
+        v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
+    if constexpr (G >= 4)
+        v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
+    if constexpr (G >= 8)
+        v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));
+    if constexpr (G >= 16)
+        v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));
+    if constexpr (G >= 32)
+        v = max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));
+    if constexpr (G >= 64) {
+        auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        v = max((uint32_t)r[0], (uint32_t)r[1]);
+    }
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Block scale of the symmetric quantizer: s = fl(a / qmax) by IEEE division.
+//
+// The per-element quotient fl(x / s) matters only through round-half-even to
+// an integer, so it is first formed as y = x * rcp(s) (v_rcp_f32, relative
+// error <= 2^-23).  With |x / s| <= qmax + 1/2, y differs from the exact
+// ratio by at most 1.5 (qmax + 1/2) 2^-23 and the IEEE quotient by at most
+// half an ulp of it: together < 2^-19.2 for qmax = 7 and < 2^-15.2 for
+// qmax = 127.  Whenever y is farther than `band` (2^-17 resp. 2^-14) from a
+// half-integer, y and the IEEE quotient lie on the same side of every
+// rounding boundary and round to the same integer.  Elements inside the band
+// -- and every element of a block whose scale is subnormal, where the
+// reciprocal is not well scaled -- take the IEEE quotient instead.  A zero
+// scale has reciprocal 0 and gives code 0.
+struct BlockScale {
+    float s;
+    float inv;
+    bool exact;
+};
+
+template <int QMAX>
+__device__ __forceinline__ BlockScale block_scale(uint32_t amax_bits) {
+    BlockScale b;
+    b.s = bitsf(amax_bits) / (float)QMAX;
+    b.exact = (b.s != 0.0f) && (b.s < 0x1p-126f);
+    b.inv = (b.s == 0.0f) ? 0.0f : __builtin_amdgcn_rcpf(b.s);
+    return b;
+}
+
+template <int QMAX>
+__device__ __forceinline__ constexpr float tie_band() {
+    static_assert(QMAX == 7 || QMAX == 127, "band derived for qmax 7 and 127 only");
+    return QMAX == 7 ? 0.5f - 0x1p-17f : 0.5f - 0x1p-14f;
+}
+
+// Fast code (before clamping); sets `redo` when the IEEE quotient must decide.
+template <int QMAX>
+__device__ __forceinline__ float code_fast(float x, const BlockScale& b, bool& redo) {
+    const float y = x * b.inv;
+    const float k = rintf(y);
+    redo |= b.exact | (__builtin_fabsf(y - k) > tie_band<QMAX>());
+    return k;
+}
+
+// Rare path: recompute with the IEEE quotient where the fast code is unsafe.
+template <int QMAX>
+__device__ __forceinline__ float code_fix(float x, const BlockScale& b, float k) {
+    const float y = x * b.inv;
+    if (b.exact || __builtin_fabsf(y - rintf(y)) > tie_band<QMAX>())
+        k = rintf(x / b.s);
+    return k;
+}
+
+template <int QMAX>
+__device__ __forceinline__ int code_clamp(float k) {
+    return (int)__builtin_fminf(__builtin_fmaxf(k, -(float)QMAX), (float)QMAX);
+}
+
+// Residual of the error-feedback quantizer and the new EF value:
+//   d = fl(k s), r = fl(c - d), e' = fl(fl(be e) + fl(br r)).
+// Built without -ffp-contract, so every product and sum rounds separately.
+__device__ __forceinline__ float ef_update(float c, int k, float s, float e, float be, float br) {
+    float d = (float)k * s;
+    float r = c - d;
+    float t1 = be * e;
+    float t2 = br * r;
+    return t1 + t2;
+}
+
+// ---------------------------------------------------------------------------
+// Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11).  Each round takes the
+// 32x32->64 products of words 0 and 2 with the two round multipliers and
+// forms the new state from their halves, the other two words and the round
+// key; the key advances by the two Weyl increments between rounds.  The key
+// is uniform across the wave, so its schedule stays in scalar registers.
+struct Philox4 {
+    uint32_t w[4];
+};
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1) {
+    constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+    constexpr uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        uint64_t p0 = (uint64_t)M0 * c0;
+        uint64_t p1 = (uint64_t)M1 * c2;
+        uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        uint32_t n1 = (uint32_t)p1;
+        uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        uint32_t n3 = (uint32_t)p0;
+        c0 = n0;
+        c1 = n1;
+        c2 = n2;
+        c3 = n3;
+        k0 += W0;
+        k1 += W1;
+    }
+    Philox4 o;
+    o.w[0] = c0;
+    o.w[1] = c1;
+    o.w[2] = c2;
+    o.w[3] = c3;
+    return o;
+}
+
+// Stochastic rounding of fp32 x to bf16 with a 16-bit random number: add it
+// below the kept 16 bits and truncate; NaN gives the canonical quiet NaN.
+__device__ __forceinline__ uint32_t sr_bf16(float x, uint32_t r16) {
+    uint32_t u = fbits(x);
+    uint32_t h = (u + r16) >> 16;
+    return (x != x) ? 0x7FC0u : h;
+}
+
+// ---------------------------------------------------------------------------
+// Launch geometry shared by the streaming kernels: a wave owns whole tiles
+// (a multiple of the quantization block), walking them with a grid stride.
+__device__ __forceinline__ size_t wave_id() {
+    return (size_t)blockIdx.x * kWavesPerWG + (threadIdx.x >> 6);
+}
+__device__ __forceinline__ size_t wave_count() { return (size_t)gridDim.x * kWavesPerWG; }
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+}  // namespace zq

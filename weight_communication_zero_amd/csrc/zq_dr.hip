@@ -1,0 +1,306 @@
+// zq_dr.hip -- qgZ receive side: dequantize P int4 chunks, reduce in fp32,
+// optionally requantize (with optional error feedback) for the next level.
+//
+// Definition ("ZeROPlusPlus.md" notes, section 1.2: gradients travel as
+// block int4 through an all-to-all, the reduction is done back in full
+// precision, inside the node first and then across nodes, with fused
+// kernels to cut latency):
+//   S = d_0 + d_1 + ... + d_{P-1}   (left to right, d_p = fl(k_p s_p))
+//   R = alpha * S;  out = R;  requant: the EF int4 quantizer applied to R.
+//
+// One pass: P * (0.5 B + 4/B B) read per output element, 4 B written when
+// out is requested, 0.5 B + 4/B B (+8 B with requant EF) for the requant.
+// In sub-vector u lane l owns the 8 outputs starting at u*512 + 8l, i.e. one
+// 32-bit word of codes per peer: each code load instruction of the wave
+// reads 256 contiguous bytes.  The sum order is fixed (ascending peer), so
+// the fp32 sums -- and the requant codes that depend on their exact bits --
+// are deterministic.  No LDS.
+#include "zq_device.h"
+#include "zq_launch.h"
+
+namespace zq {
+namespace {
+
+template <int B>
+struct DrGeom {
+    static constexpr int VEC = 8;
+    static constexpr int SUB = kWave * VEC;
+    static constexpr int LPB = B <= SUB ? B / VEC : kWave;
+    static constexpr int SPB = B <= SUB ? 1 : B / SUB;
+    static constexpr int U = SPB > 2 ? SPB : 2;
+    static constexpr int TILE = SUB * U;
+    static constexpr int BPT = TILE / B;
+};
+
+// Signed value of nibble j of a code word (shift it to the top, then an
+// arithmetic shift back down sign-extends it).
+__device__ __forceinline__ float nib(uint32_t w, int j) {
+    return (float)((int32_t)(w << (28 - 4 * j)) >> 28);
+}
+
+// Up to 4 code bytes starting at byte offset ob, only those below nbytes.
+__device__ __forceinline__ uint32_t load_code_word_masked(const uint8_t* p, size_t ob,
+                                                          size_t nbytes) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        if (ob + b < nbytes)
+            w |= (uint32_t)p[ob + b] << (8 * b);
+    return w;
+}
+
+template <int B, int PMAX, bool OUT, bool RQ, bool MASK>
+__device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
+    const bool RQEF = RQ && p.rq_ef != nullptr;
+    using G = DrGeom<B>;
+    const int lane = lane_id();
+    const size_t base = tile * (size_t)G::TILE;
+    const size_t n = p.n;
+    const size_t nbytes = (n + 1) / 2;
+
+    uint32_t cw[PMAX][G::U];
+    float sc[PMAX][G::U];
+    float e2[G::U][8];
+
+    // Issue every load of the tile first.
+#pragma unroll
+    for (int q = 0; q < PMAX; ++q) {
+        if (q < (int)p.P) {
+#pragma unroll
+            for (int u = 0; u < G::U; ++u) {
+                const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * 8;
+                if constexpr (!MASK) {
+                    cw[q][u] = __builtin_nontemporal_load((const uint32_t*)(p.codes[q] + i0 / 2));
+                    sc[q][u] = p.scales[q][i0 / B];
+                } else {
+                    cw[q][u] = load_code_word_masked(p.codes[q], i0 / 2, nbytes);
+                    sc[q][u] = i0 < n ? p.scales[q][i0 / B] : 0.0f;
+                }
+            }
+        }
+    }
+    if (RQEF) {
+#pragma unroll
+        for (int u = 0; u < G::U; ++u) {
+            const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * 8;
+            if constexpr (!MASK) {
+                f4 a = __builtin_nontemporal_load((const f4*)(p.rq_ef + i0));
+                f4 b = __builtin_nontemporal_load((const f4*)(p.rq_ef + i0 + 4));
+                e2[u][0] = a.x; e2[u][1] = a.y; e2[u][2] = a.z; e2[u][3] = a.w;
+                e2[u][4] = b.x; e2[u][5] = b.y; e2[u][6] = b.z; e2[u][7] = b.w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    e2[u][j] = i0 + j < n ? p.rq_ef[i0 + j] : 0.0f;
+            }
+        }
+    }
+
+    // Dequantize and reduce, ascending peer order.
+    float R[G::U][8];
+#pragma unroll
+    for (int u = 0; u < G::U; ++u) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float S = nib(cw[0][u], j) * sc[0][u];
+#pragma unroll
+            for (int q = 1; q < PMAX; ++q)
+                if (q < (int)p.P)
+                    S = S + nib(cw[q][u], j) * sc[q][u];
+            R[u][j] = p.alpha * S;
+        }
+    }
+
+    if constexpr (OUT) {
+#pragma unroll
+        for (int u = 0; u < G::U; ++u) {
+            const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * 8;
+            if constexpr (!MASK) {
+                f4 a = {R[u][0], R[u][1], R[u][2], R[u][3]};
+                f4 b = {R[u][4], R[u][5], R[u][6], R[u][7]};
+                __builtin_nontemporal_store(a, (f4*)(p.out + i0));
+                __builtin_nontemporal_store(b, (f4*)(p.out + i0 + 4));
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (i0 + j < n)
+                        p.out[i0 + j] = R[u][j];
+            }
+        }
+    }
+
+    if constexpr (RQ) {
+        float c[G::U][8];
+#pragma unroll
+        for (int u = 0; u < G::U; ++u)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                c[u][j] = RQEF ? R[u][j] + e2[u][j] : R[u][j];
+        // Beyond n the value must not enter the block max.
+        if constexpr (MASK) {
+#pragma unroll
+            for (int u = 0; u < G::U; ++u) {
+                const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * 8;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (i0 + j >= n)
+                        c[u][j] = 0.0f;
+            }
+        }
+        BlockScale bs[G::SPB == 1 ? G::U : G::BPT];
+        if constexpr (G::SPB == 1) {
+#pragma unroll
+            for (int u = 0; u < G::U; ++u) {
+                uint32_t m = 0;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    m = max(m, absbits(c[u][j]));
+                bs[u] = block_scale<7>(group_max<G::LPB>(m));
+            }
+        } else {
+#pragma unroll
+            for (int b = 0; b < G::BPT; ++b) {
+                uint32_t m = 0;
+#pragma unroll
+                for (int u = b * G::SPB; u < (b + 1) * G::SPB; ++u)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        m = max(m, absbits(c[u][j]));
+                bs[b] = block_scale<7>(group_max<kWave>(m));
+            }
+        }
+        if constexpr (G::SPB == 1) {
+            if (lane % G::LPB == 0) {
+#pragma unroll
+                for (int u = 0; u < G::U; ++u) {
+                    const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * 8;
+                    if (!MASK || i0 < n)
+                        p.rq_scales[i0 / B] = bs[u].s;
+                }
+            }
+        } else {
+            if (lane == 0) {
+#pragma unroll
+                for (int b = 0; b < G::BPT; ++b) {
+                    const size_t i0 = base + (size_t)b * B;
+                    if (!MASK || i0 < n)
+                        p.rq_scales[i0 / B] = bs[b].s;
+                }
+            }
+        }
+        float kf[G::U][8];
+        bool redo = false;
+#pragma unroll
+        for (int u = 0; u < G::U; ++u)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                kf[u][j] = code_fast<7>(c[u][j], bs[G::SPB == 1 ? u : u / G::SPB], redo);
+        if (redo) {
+#pragma unroll
+            for (int u = 0; u < G::U; ++u)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    kf[u][j] = code_fix<7>(c[u][j], bs[G::SPB == 1 ? u : u / G::SPB], kf[u][j]);
+        }
+#pragma unroll
+        for (int u = 0; u < G::U; ++u) {
+            const BlockScale& s = bs[G::SPB == 1 ? u : u / G::SPB];
+            const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * 8;
+            uint32_t packed = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int k = code_clamp<7>(kf[u][j]);
+                packed |= ((uint32_t)k & 0xFu) << (4 * j);
+                if (RQEF)
+                    e2[u][j] = ef_update(c[u][j], k, s.s, e2[u][j], p.rq_beta_e, p.rq_beta_r);
+            }
+            if constexpr (!MASK) {
+                __builtin_nontemporal_store(packed, (uint32_t*)(p.rq_codes + i0 / 2));
+                if (RQEF) {
+                    f4 a = {e2[u][0], e2[u][1], e2[u][2], e2[u][3]};
+                    f4 b = {e2[u][4], e2[u][5], e2[u][6], e2[u][7]};
+                    __builtin_nontemporal_store(a, (f4*)(p.rq_ef + i0));
+                    __builtin_nontemporal_store(b, (f4*)(p.rq_ef + i0 + 4));
+                }
+            } else {
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    if (i0 + 2 * b < n)
+                        p.rq_codes[i0 / 2 + b] = (uint8_t)(packed >> (8 * b));
+                if (RQEF) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        if (i0 + j < n)
+                            p.rq_ef[i0 + j] = e2[u][j];
+                }
+            }
+        }
+    }
+}
+
+// PMAX: the kernel serves every P <= PMAX; only PMAX pointer pairs stay
+// live, so the common P = 4 / 8 cases keep their pointers in SGPRs.
+template <int B, int PMAX, bool OUT, bool RQ>
+__global__ __launch_bounds__(kBlockThreads) void dr_kernel(DrParams p) {
+    using G = DrGeom<B>;
+    const size_t ntiles = (p.n + G::TILE - 1) / G::TILE;
+    const size_t nfull = p.n / G::TILE;
+    for (size_t t = wave_id(); t < ntiles; t += wave_count()) {
+        if (t < nfull)
+            dr_tile<B, PMAX, OUT, RQ, false>(p, t);
+        else
+            dr_tile<B, PMAX, OUT, RQ, true>(p, t);
+    }
+}
+
+template <int B, int PMAX, bool OUT, bool RQ>
+hipError_t launch_b(const DrParams& p, hipStream_t stream) {
+    using G = DrGeom<B>;
+    const size_t tiles = (p.n + G::TILE - 1) / G::TILE;
+    DrParams arg = p;
+    void* args[] = {(void*)&arg};
+    return hipLaunchKernel((const void*)&dr_kernel<B, PMAX, OUT, RQ>,
+                           dim3(grid_for_tiles(tiles, kWavesPerWG)), dim3(kBlockThreads), args, 0,
+                           stream);
+}
+
+template <int B, int PMAX>
+hipError_t launch_flags(const DrParams& p, hipStream_t st) {
+    const bool out = p.out != nullptr, rq = p.rq_codes != nullptr;
+    if (out && !rq)
+        return launch_b<B, PMAX, true, false>(p, st);
+    if (!out && rq)
+        return launch_b<B, PMAX, false, true>(p, st);
+    if (out && rq)
+        return launch_b<B, PMAX, true, true>(p, st);
+    return hipErrorInvalidValue;
+}
+
+template <int B>
+hipError_t launch_peers(const DrParams& p, hipStream_t st) {
+    if (p.P <= 2)
+        return launch_flags<B, 2>(p, st);
+    if (p.P <= 4)
+        return launch_flags<B, 4>(p, st);
+    if (p.P <= 8)
+        return launch_flags<B, 8>(p, st);
+    return launch_flags<B, 16>(p, st);
+}
+
+}  // namespace
+
+hipError_t launch_dequant_reduce(const DrParams& p, uint32_t block, hipStream_t st) {
+    switch (block) {
+        case 32: return launch_peers<32>(p, st);
+        case 64: return launch_peers<64>(p, st);
+        case 128: return launch_peers<128>(p, st);
+        case 256: return launch_peers<256>(p, st);
+        case 512: return launch_peers<512>(p, st);
+        case 1024: return launch_peers<1024>(p, st);
+        case 2048: return launch_peers<2048>(p, st);
+        case 4096: return launch_peers<4096>(p, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace zq

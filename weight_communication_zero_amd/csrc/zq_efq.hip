@@ -1,0 +1,237 @@
+// zq_efq.hip -- block int4 gradient quantization with LoCo error feedback.
+//
+// Definition ("Merge LoCo with Zero++", Overview: error feedback applied to
+// the 4-bit gradients before communication; review thread: one EF buffer per
+// parameter.  "ZeROPlusPlus.md" notes, section 1.2: qgZ block int4):
+//   c = g + e;  s = absmax(c over the block) / 7;  k = clamp(rne(c / s), +-7)
+//   e' = beta_e * e + beta_r * (c - k s)          (every step rounded in fp32)
+//
+// One pass over HBM: read g (4 or 2 B/elem) and e (4 B), write e (4 B),
+// codes (0.5 B) and one fp32 scale per block.  Layout on the wave: a wave
+// owns a tile of U sub-vectors of 256 elements; in sub-vector u lane l holds
+// the 4 consecutive elements starting at u*256 + 4l, so every load and store
+// instruction of the wave covers one contiguous span (1 KB of fp32).  A block
+// of B <= 256 elements is B/4 adjacent lanes of one sub-vector (absmax by a
+// DPP butterfly inside the lane group); a larger block is B/256 whole
+// sub-vectors (in-lane max first, then the full-wave butterfly).  No LDS.
+#include "zq_device.h"
+#include "zq_launch.h"
+
+namespace zq {
+namespace {
+
+template <int B>
+struct EfqGeom {
+    static constexpr int VEC = 4;
+    static constexpr int SUB = kWave * VEC;
+    static constexpr int LPB = B <= SUB ? B / VEC : kWave;
+    static constexpr int SPB = B <= SUB ? 1 : B / SUB;
+    static constexpr int U = SPB > 4 ? SPB : 4;
+    static constexpr int TILE = SUB * U;
+    static constexpr int BPT = TILE / B;
+};
+
+template <bool BF16, bool EF, int B, bool MASK>
+__device__ __forceinline__ void efq_tile(const void* __restrict__ gv, float* __restrict__ ef,
+                                         size_t n, float beta_e, float beta_r,
+                                         uint8_t* __restrict__ codes, float* __restrict__ scales,
+                                         size_t tile) {
+    using G = EfqGeom<B>;
+    const int lane = lane_id();
+    const size_t base = tile * (size_t)G::TILE;
+
+    float c[G::U][4];
+    float e[G::U][4];
+
+#pragma unroll
+    for (int u = 0; u < G::U; ++u) {
+        const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * 4;
+        float gv4[4];
+        if constexpr (!MASK) {
+            if constexpr (BF16) {
+                u2 w = __builtin_nontemporal_load((const u2*)((const uint16_t*)gv + i0));
+                gv4[0] = bf16lo(w.x);
+                gv4[1] = bf16hi(w.x);
+                gv4[2] = bf16lo(w.y);
+                gv4[3] = bf16hi(w.y);
+            } else {
+                f4 w = __builtin_nontemporal_load((const f4*)((const float*)gv + i0));
+                gv4[0] = w.x;
+                gv4[1] = w.y;
+                gv4[2] = w.z;
+                gv4[3] = w.w;
+            }
+            if constexpr (EF) {
+                f4 v = __builtin_nontemporal_load((const f4*)(ef + i0));
+                e[u][0] = v.x;
+                e[u][1] = v.y;
+                e[u][2] = v.z;
+                e[u][3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool in = i0 + j < n;
+                if constexpr (BF16)
+                    gv4[j] = in ? bf16lo(((const uint16_t*)gv)[i0 + j]) : 0.0f;
+                else
+                    gv4[j] = in ? ((const float*)gv)[i0 + j] : 0.0f;
+                if constexpr (EF)
+                    e[u][j] = in ? ef[i0 + j] : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            c[u][j] = EF ? gv4[j] + e[u][j] : gv4[j];
+    }
+
+    // Block absmax and scale.
+    BlockScale bs[G::SPB == 1 ? G::U : G::BPT];
+    if constexpr (G::SPB == 1) {
+#pragma unroll
+        for (int u = 0; u < G::U; ++u) {
+            uint32_t m = max(max(absbits(c[u][0]), absbits(c[u][1])),
+                             max(absbits(c[u][2]), absbits(c[u][3])));
+            bs[u] = block_scale<7>(group_max<G::LPB>(m));
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < G::BPT; ++b) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int u = b * G::SPB; u < (b + 1) * G::SPB; ++u)
+                m = max(m, max(max(absbits(c[u][0]), absbits(c[u][1])),
+                               max(absbits(c[u][2]), absbits(c[u][3]))));
+            bs[b] = block_scale<7>(group_max<kWave>(m));
+        }
+    }
+
+    // Scales: one writer lane per block.
+    if constexpr (G::SPB == 1) {
+        if (lane % G::LPB == 0) {
+#pragma unroll
+            for (int u = 0; u < G::U; ++u) {
+                const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * 4;
+                if (!MASK || i0 < n)
+                    scales[i0 / B] = bs[u].s;
+            }
+        }
+    } else {
+        if (lane == 0) {
+#pragma unroll
+            for (int b = 0; b < G::BPT; ++b) {
+                const size_t i0 = base + (size_t)b * B;
+                if (!MASK || i0 < n)
+                    scales[i0 / B] = bs[b].s;
+            }
+        }
+    }
+
+    // Codes: fast reciprocal path for the whole tile, one rare fix-up branch.
+    float kf[G::U][4];
+    bool redo = false;
+#pragma unroll
+    for (int u = 0; u < G::U; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            kf[u][j] = code_fast<7>(c[u][j], bs[G::SPB == 1 ? u : u / G::SPB], redo);
+    if (redo) {
+#pragma unroll
+        for (int u = 0; u < G::U; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                kf[u][j] = code_fix<7>(c[u][j], bs[G::SPB == 1 ? u : u / G::SPB], kf[u][j]);
+    }
+
+    // Residual, EF update, packing, stores.
+#pragma unroll
+    for (int u = 0; u < G::U; ++u) {
+        const BlockScale& sc = bs[G::SPB == 1 ? u : u / G::SPB];
+        const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * 4;
+        uint32_t packed = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k = code_clamp<7>(kf[u][j]);
+            packed |= ((uint32_t)k & 0xFu) << (4 * j);
+            if constexpr (EF)
+                e[u][j] = ef_update(c[u][j], k, sc.s, e[u][j], beta_e, beta_r);
+        }
+        if constexpr (!MASK) {
+            __builtin_nontemporal_store((uint16_t)packed, (uint16_t*)(codes + i0 / 2));
+            if constexpr (EF) {
+                f4 v = {e[u][0], e[u][1], e[u][2], e[u][3]};
+                __builtin_nontemporal_store(v, (f4*)(ef + i0));
+            }
+        } else {
+            if (i0 < n)
+                codes[i0 / 2] = (uint8_t)(packed & 0xFFu);
+            if (i0 + 2 < n)
+                codes[i0 / 2 + 1] = (uint8_t)(packed >> 8);
+            if constexpr (EF) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (i0 + j < n)
+                        ef[i0 + j] = e[u][j];
+            }
+        }
+    }
+}
+
+template <bool BF16, bool EF, int B>
+__global__ __launch_bounds__(kBlockThreads) void efq_kernel(const void* __restrict__ g,
+                                                            float* __restrict__ ef, size_t n,
+                                                            float beta_e, float beta_r,
+                                                            uint8_t* __restrict__ codes,
+                                                            float* __restrict__ scales) {
+    using G = EfqGeom<B>;
+    const size_t ntiles = (n + G::TILE - 1) / G::TILE;
+    const size_t nfull = n / G::TILE;
+    for (size_t t = wave_id(); t < ntiles; t += wave_count()) {
+        if (t < nfull)
+            efq_tile<BF16, EF, B, false>(g, ef, n, beta_e, beta_r, codes, scales, t);
+        else
+            efq_tile<BF16, EF, B, true>(g, ef, n, beta_e, beta_r, codes, scales, t);
+    }
+}
+
+template <bool BF16, bool EF, int B>
+hipError_t launch_b(const void* g, float* ef, size_t n, float beta_e, float beta_r,
+                    uint8_t* codes, float* scales, hipStream_t stream) {
+    using G = EfqGeom<B>;
+    const size_t tiles = (n + G::TILE - 1) / G::TILE;
+    void* args[] = {(void*)&g, (void*)&ef, (void*)&n, (void*)&beta_e, (void*)&beta_r,
+                    (void*)&codes, (void*)&scales};
+    return hipLaunchKernel((const void*)&efq_kernel<BF16, EF, B>,
+                           dim3(grid_for_tiles(tiles, kWavesPerWG)), dim3(kBlockThreads), args, 0,
+                           stream);
+}
+
+template <bool BF16, bool EF>
+hipError_t launch_t(const void* g, float* ef, size_t n, uint32_t block, float be, float br,
+                    uint8_t* codes, float* scales, hipStream_t st) {
+    switch (block) {
+        case 32: return launch_b<BF16, EF, 32>(g, ef, n, be, br, codes, scales, st);
+        case 64: return launch_b<BF16, EF, 64>(g, ef, n, be, br, codes, scales, st);
+        case 128: return launch_b<BF16, EF, 128>(g, ef, n, be, br, codes, scales, st);
+        case 256: return launch_b<BF16, EF, 256>(g, ef, n, be, br, codes, scales, st);
+        case 512: return launch_b<BF16, EF, 512>(g, ef, n, be, br, codes, scales, st);
+        case 1024: return launch_b<BF16, EF, 1024>(g, ef, n, be, br, codes, scales, st);
+        case 2048: return launch_b<BF16, EF, 2048>(g, ef, n, be, br, codes, scales, st);
+        case 4096: return launch_b<BF16, EF, 4096>(g, ef, n, be, br, codes, scales, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_ef_int4(const void* g, bool g_bf16, float* ef, size_t n, uint32_t block,
+                                   float beta_e, float beta_r, uint8_t* codes, float* scales,
+                                   hipStream_t stream) {
+    if (g_bf16)
+        return ef ? launch_t<true, true>(g, ef, n, block, beta_e, beta_r, codes, scales, stream)
+                  : launch_t<true, false>(g, ef, n, block, beta_e, beta_r, codes, scales, stream);
+    return ef ? launch_t<false, true>(g, ef, n, block, beta_e, beta_r, codes, scales, stream)
+              : launch_t<false, false>(g, ef, n, block, beta_e, beta_r, codes, scales, stream);
+}
+
+}  // namespace zq

@@ -1,0 +1,139 @@
+// zq_sr.hip -- bf16 gradient accumulation with stochastic rounding.
+//
+// Definition ("Zero 2 #593", review of llmc/cuda_utils.cuh: the accumulation
+// adds the two bf16 values in fp32 and rounds the sum stochastically so it
+// stays correct in expectation; review of llmc/zero.cuh: zeroing the reduced
+// buffer can be folded into the same kernel):
+//   x = float(dst) + float(src);  dst = SR_bf16(x, r16(seed, counter_base + i))
+// r16 comes from Philox-4x32-10 at counter (q >> 3): one call gives the
+// eight 16-bit numbers of indices 8c .. 8c+7.
+//
+// 6 B/elem (8 with zero_src).  In sub-vector u lane l owns the 8 elements
+// starting at u*512 + 8l: one 16-byte load of dst and of src, one Philox
+// call (two when counter_base is not a multiple of 8), one 16-byte store.
+#include "zq_device.h"
+#include "zq_launch.h"
+
+namespace zq {
+namespace {
+
+constexpr int kSrU = 2;
+constexpr int kSrSub = kWave * 8;
+constexpr int kSrTile = kSrSub * kSrU;
+
+// The random numbers of the 8 indices q0 .. q0+7 where q0 = 8*c + PHASE.
+template <int PHASE>
+__device__ __forceinline__ void r16x8(uint64_t c, uint32_t k0, uint32_t k1, uint32_t r[8]) {
+    const Philox4 a = philox4x32_10((uint32_t)c, (uint32_t)(c >> 32), 0u, 0u, k0, k1);
+    Philox4 b = a;
+    if constexpr (PHASE != 0) {
+        const uint64_t c1 = c + 1;
+        b = philox4x32_10((uint32_t)c1, (uint32_t)(c1 >> 32), 0u, 0u, k0, k1);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int qq = PHASE + j;
+        const uint32_t word = qq < 8 ? a.w[(qq & 7) >> 1] : b.w[(qq & 7) >> 1];
+        r[j] = (qq & 1) ? (word >> 16) : (word & 0xFFFFu);
+    }
+}
+
+template <int PHASE, bool ZERO, bool MASK>
+__device__ __forceinline__ void sr_tile(uint16_t* __restrict__ dst, uint16_t* __restrict__ src,
+                                        size_t n, uint32_t k0, uint32_t k1, uint64_t cbase8,
+                                        size_t tile) {
+    const int lane = lane_id();
+    const size_t base = tile * (size_t)kSrTile;
+    u4 d[kSrU], s[kSrU];
+#pragma unroll
+    for (int u = 0; u < kSrU; ++u) {
+        const size_t i0 = base + (size_t)u * kSrSub + (size_t)lane * 8;
+        if constexpr (!MASK) {
+            d[u] = __builtin_nontemporal_load((const u4*)(dst + i0));
+            s[u] = __builtin_nontemporal_load((const u4*)(src + i0));
+        } else {
+            uint32_t dv[4] = {0, 0, 0, 0}, sv[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (i0 + j < n) {
+                    dv[j >> 1] |= (uint32_t)dst[i0 + j] << (16 * (j & 1));
+                    sv[j >> 1] |= (uint32_t)src[i0 + j] << (16 * (j & 1));
+                }
+            d[u] = u4{dv[0], dv[1], dv[2], dv[3]};
+            s[u] = u4{sv[0], sv[1], sv[2], sv[3]};
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kSrU; ++u) {
+        const size_t i0 = base + (size_t)u * kSrSub + (size_t)lane * 8;
+        uint32_t r[8];
+        r16x8<PHASE>(cbase8 + (i0 >> 3), k0, k1, r);
+        const uint32_t dw[4] = {d[u].x, d[u].y, d[u].z, d[u].w};
+        const uint32_t sw[4] = {s[u].x, s[u].y, s[u].z, s[u].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const float x0 = bf16lo(dw[h]) + bf16lo(sw[h]);
+            const float x1 = bf16hi(dw[h]) + bf16hi(sw[h]);
+            o[h] = sr_bf16(x0, r[2 * h]) | (sr_bf16(x1, r[2 * h + 1]) << 16);
+        }
+        if constexpr (!MASK) {
+            __builtin_nontemporal_store(u4{o[0], o[1], o[2], o[3]}, (u4*)(dst + i0));
+            if constexpr (ZERO)
+                __builtin_nontemporal_store(u4{0u, 0u, 0u, 0u}, (u4*)(src + i0));
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (i0 + j < n) {
+                    dst[i0 + j] = (uint16_t)(o[j >> 1] >> (16 * (j & 1)));
+                    if constexpr (ZERO)
+                        src[i0 + j] = 0;
+                }
+        }
+    }
+}
+
+template <int PHASE, bool ZERO>
+__global__ __launch_bounds__(kBlockThreads) void sr_kernel(uint16_t* __restrict__ dst,
+                                                           uint16_t* __restrict__ src, size_t n,
+                                                           uint32_t k0, uint32_t k1,
+                                                           uint64_t cbase8) {
+    const size_t ntiles = (n + kSrTile - 1) / kSrTile;
+    const size_t nfull = n / kSrTile;
+    for (size_t t = wave_id(); t < ntiles; t += wave_count()) {
+        if (t < nfull)
+            sr_tile<PHASE, ZERO, false>(dst, src, n, k0, k1, cbase8, t);
+        else
+            sr_tile<PHASE, ZERO, true>(dst, src, n, k0, k1, cbase8, t);
+    }
+}
+
+template <int PHASE>
+const void* sr_fn(bool zero) {
+    return zero ? (const void*)&sr_kernel<PHASE, true> : (const void*)&sr_kernel<PHASE, false>;
+}
+
+}  // namespace
+
+hipError_t launch_sr_accumulate(uint16_t* dst, uint16_t* src, size_t n, uint64_t seed,
+                                uint64_t counter_base, bool zero_src, hipStream_t stream) {
+    const void* fn = nullptr;
+    switch (counter_base & 7u) {
+        case 0: fn = sr_fn<0>(zero_src); break;
+        case 1: fn = sr_fn<1>(zero_src); break;
+        case 2: fn = sr_fn<2>(zero_src); break;
+        case 3: fn = sr_fn<3>(zero_src); break;
+        case 4: fn = sr_fn<4>(zero_src); break;
+        case 5: fn = sr_fn<5>(zero_src); break;
+        case 6: fn = sr_fn<6>(zero_src); break;
+        default: fn = sr_fn<7>(zero_src); break;
+    }
+    uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    uint64_t cbase8 = counter_base >> 3;
+    const size_t tiles = (n + kSrTile - 1) / kSrTile;
+    void* args[] = {(void*)&dst, (void*)&src, (void*)&n, (void*)&k0, (void*)&k1, (void*)&cbase8};
+    return hipLaunchKernel(fn, dim3(grid_for_tiles(tiles, kWavesPerWG)), dim3(kBlockThreads), args,
+                           0, stream);
+}
+
+}  // namespace zq

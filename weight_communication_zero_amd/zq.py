@@ -1,0 +1,203 @@
+"""ctypes binding of libzq (include/zq.h): argument marshalling only.
+
+Every function takes torch tensors (device memory) or raw integer device
+pointers, converts them to the C ABI's plain pointers and sizes, passes the
+current torch HIP stream unless one is given, and raises ``ZQError`` on a
+non-OK status.  All arithmetic happens in libzq's HIP kernels; there is no
+fallback path: if ``libzq.so`` is missing or cannot be loaded, importing this
+module fails.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import torch  # loaded first: libzq then binds to the HIP runtime torch uses
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzq.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "zq.h")
+
+ZQ_FP32, ZQ_BF16 = 0, 1
+
+STATUS = {
+    0: "ZQ_OK", 1: "ZQ_ERR_NULL", 2: "ZQ_ERR_SIZE", 3: "ZQ_ERR_BLOCK", 4: "ZQ_ERR_ALIGN",
+    5: "ZQ_ERR_ALIAS", 6: "ZQ_ERR_PEERS", 7: "ZQ_ERR_DTYPE", 8: "ZQ_ERR_LAUNCH",
+}
+ZQ_OK, ZQ_ERR_NULL, ZQ_ERR_SIZE, ZQ_ERR_BLOCK, ZQ_ERR_ALIGN = 0, 1, 2, 3, 4
+ZQ_ERR_ALIAS, ZQ_ERR_PEERS, ZQ_ERR_DTYPE, ZQ_ERR_LAUNCH = 5, 6, 7, 8
+
+
+class ZQError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {lib.zq_status_str(status).decode()}")
+        self.status = status
+
+
+def _load() -> C.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; build it with `python -c 'import __graft_entry__ as g; g.build()'`"
+            " (hipcc, gfx950)")
+    L = C.CDLL(LIB_PATH)
+    vp, sz, u32, u64, f32, i32 = C.c_void_p, C.c_size_t, C.c_uint32, C.c_uint64, C.c_float, C.c_int
+    L.zq_quantize_ef_int4.argtypes = [vp, i32, vp, sz, u32, f32, f32, vp, vp, vp]
+    L.zq_dequant_reduce.argtypes = [u32, vp, vp, sz, u32, f32, vp, vp, vp, vp, f32, f32, vp]
+    L.zq_quant_int8.argtypes = [vp, i32, sz, u32, vp, vp, vp]
+    L.zq_dequant_int8.argtypes = [vp, vp, sz, u32, vp, i32, vp]
+    L.zq_sr_accumulate.argtypes = [vp, vp, sz, u64, u64, i32, vp]
+    for f in ("zq_quantize_ef_int4", "zq_dequant_reduce", "zq_quant_int8", "zq_dequant_int8",
+              "zq_sr_accumulate"):
+        getattr(L, f).restype = i32
+    L.zq_int4_code_bytes.argtypes = [sz]
+    L.zq_int4_code_bytes.restype = sz
+    L.zq_num_blocks.argtypes = [sz, u32]
+    L.zq_num_blocks.restype = sz
+    L.zq_status_str.argtypes = [i32]
+    L.zq_status_str.restype = C.c_char_p
+    L.zq_abi_version.argtypes = []
+    L.zq_abi_version.restype = u32
+    return L
+
+
+lib = _load()
+
+
+def declared_symbols() -> list[str]:
+    """Function names declared in include/zq.h."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:zq_status|size_t|const char \*|uint32_t)\s*\*?\s*(zq_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def _p(x) -> int | None:
+    """Device pointer of a tensor (or an int already a pointer; None -> NULL)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not x.is_contiguous():
+        raise ValueError("libzq needs contiguous tensors")
+    return x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dtype(t) -> int:
+    if t.dtype == torch.float32:
+        return ZQ_FP32
+    if t.dtype == torch.bfloat16:
+        return ZQ_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(name: str, t, numel: int, dtypes) -> None:
+    """Host-side guard before any launch: a tensor argument must be a
+    contiguous GPU tensor of an accepted dtype holding at least `numel`
+    elements, so no kernel can index past a caller's buffer."""
+    if t is None or isinstance(t, int):
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+
+
+_F32 = (torch.float32,)
+_BF16 = (torch.bfloat16,)
+_FLOAT = (torch.float32, torch.bfloat16)
+_U8 = (torch.uint8,)
+_I8 = (torch.int8,)
+
+
+def _check(fn: str, st: int) -> None:
+    if st != ZQ_OK:
+        raise ZQError(fn, st)
+
+
+def int4_code_bytes(n: int) -> int:
+    return lib.zq_int4_code_bytes(n)
+
+
+def num_blocks(n: int, block: int) -> int:
+    return lib.zq_num_blocks(n, block)
+
+
+def zq_quantize_ef_int4(g, ef, block: int, beta_e: float, beta_r: float, codes, scales,
+                        stream=None, n: int | None = None) -> None:
+    """EF int4 quantize: g (fp32/bf16), ef (fp32 or None, updated in place)
+    -> codes (uint8, ceil(n/2)), scales (fp32, ceil(n/block))."""
+    n = g.numel() if n is None else n
+    nb = (n + block - 1) // block if block > 0 else 0
+    _need("g", g, n, _FLOAT)
+    _need("ef", ef, n, _F32)
+    _need("codes", codes, (n + 1) // 2, _U8)
+    _need("scales", scales, nb, _F32)
+    _check("zq_quantize_ef_int4",
+           lib.zq_quantize_ef_int4(_p(g), _dtype(g), _p(ef), n, block, beta_e, beta_r, _p(codes),
+                                   _p(scales), _stream(stream)))
+
+
+def zq_dequant_reduce(codes_list, scales_list, n_chunk: int, block: int, alpha: float, out=None,
+                      rq_codes=None, rq_scales=None, rq_ef=None, rq_beta_e: float = 0.0,
+                      rq_beta_r: float = 1.0, stream=None) -> None:
+    """Dequantize P int4 chunks, reduce in fp32 (times alpha) into out, and /
+    or requantize into rq_codes / rq_scales (with optional rq_ef)."""
+    P = len(codes_list)
+    if P != len(scales_list):
+        raise ValueError("codes_list and scales_list differ in length")
+    nb = (n_chunk + block - 1) // block if block > 0 else 0
+    for c, sc in zip(codes_list, scales_list):
+        _need("codes[p]", c, (n_chunk + 1) // 2, _U8)
+        _need("scales[p]", sc, nb, _F32)
+    _need("out", out, n_chunk, _F32)
+    _need("rq_codes", rq_codes, (n_chunk + 1) // 2, _U8)
+    _need("rq_scales", rq_scales, nb, _F32)
+    _need("rq_ef", rq_ef, n_chunk, _F32)
+    cp = (C.c_void_p * max(P, 1))(*[_p(c) for c in codes_list])
+    sp = (C.c_void_p * max(P, 1))(*[_p(s) for s in scales_list])
+    _check("zq_dequant_reduce",
+           lib.zq_dequant_reduce(P, cp, sp, n_chunk, block, alpha, _p(out), _p(rq_codes),
+                                 _p(rq_scales), _p(rq_ef), rq_beta_e, rq_beta_r, _stream(stream)))
+
+
+def zq_quant_int8(w, block: int, codes, scales, stream=None, n: int | None = None) -> None:
+    n = w.numel() if n is None else n
+    _need("w", w, n, _FLOAT)
+    _need("codes", codes, n, _I8)
+    _need("scales", scales, (n + block - 1) // block if block > 0 else 0, _F32)
+    _check("zq_quant_int8",
+           lib.zq_quant_int8(_p(w), _dtype(w), n, block, _p(codes), _p(scales), _stream(stream)))
+
+
+def zq_dequant_int8(codes, scales, block: int, out, stream=None, n: int | None = None) -> None:
+    n = codes.numel() if n is None else n
+    _need("codes", codes, n, _I8)
+    _need("scales", scales, (n + block - 1) // block if block > 0 else 0, _F32)
+    _need("out", out, n, _FLOAT)
+    _check("zq_dequant_int8",
+           lib.zq_dequant_int8(_p(codes), _p(scales), n, block, _p(out), _dtype(out),
+                               _stream(stream)))
+
+
+def zq_sr_accumulate(dst, src, seed: int, counter_base: int = 0, zero_src: bool = False,
+                     stream=None, n: int | None = None) -> None:
+    """bf16 dst += src with stochastic rounding (dst, src: torch.bfloat16)."""
+    n = dst.numel() if n is None else n
+    _need("dst", dst, n, _BF16)
+    _need("src", src, n, _BF16)
+    _check("zq_sr_accumulate",
+           lib.zq_sr_accumulate(_p(dst), _p(src), n, seed, counter_base, 1 if zero_src else 0,
+                                _stream(stream)))
