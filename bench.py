@@ -1,0 +1,417 @@
+"""Benchmark of the qgZ + LoCo data-parallel hot path on one MI355X.
+
+Workload (one step = one pass of the whole gradient path over one batch):
+one GPU's share of a ~7.5B Llama-2-style fp32 gradient (36 layers, hidden
+4096, FFN 11008, vocab 32000: 7,547,949,056 elements, heavy-tailed embedding,
+lm_head and first/last block), i.e. the two-level qgZ of "ZeROPlusPlus.md"
+(section 1.2) with LoCo error feedback ("Merge LoCo with Zero++", Overview):
+  1. EF int4 quantize of the whole gradient, block 128, beta 0.9;
+  2. 8-way dequantize-reduce-requantize of the intra-node chunk (M/8 elements);
+  3. 4-way dequantize-reduce of the inter-node sub-chunk (M/32), alpha 1/32.
+On one GPU the exchanges are identities: this GPU's own 8 chunks (resp. 4
+sub-chunks) stand in for the peers' chunks -- same shapes, same bytes.
+
+value = algorithmic bytes of one step / measured step time (inputs resident
+in HBM).  The same run also times the other kernels of the path on their own
+workloads (int8 weight quantize/dequantize of a ~0.85B model, stochastic-
+rounding accumulation of GPT-2 124M gradients, the 0.85B EF-quantize + 8-way
+reduce, the 4-rank bf16 case) and the CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "effective HBM GB/s (and % of peak) for EF-int4 quantize + P-way dequant-reduce"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-rows", action="store_true", help="skip the per-row extra workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-sample-elems", type=int, default=3 << 30,
+                    help="gradient elements the CPU oracle processes (a multiple of 4096)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after the timed steps, run a 1 GiB fp32 copy (known HBM bytes) so that "
+                         "rocprofv3 memory counters can be scaled")
+    ap.add_argument("--summarize-rocprof", metavar="DIR",
+                    help="print a summary of the rocprofv3 CSV output under DIR and exit")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------- byte counts --
+
+def efq_bytes(n, block, g_bytes, ef=True):
+    return n * (g_bytes + (8 if ef else 0) + 0.5) + 4 * math.ceil(n / block)
+
+
+def dr_bytes(n, block, P, out=True, rq=False, rq_ef=False):
+    per_chunk = 0.5 * n + 4 * math.ceil(n / block)
+    b = P * per_chunk
+    if out:
+        b += 4 * n
+    if rq:
+        b += per_chunk
+    if rq_ef:
+        b += 8 * n
+    return b
+
+
+class EventTimer:
+    """HIP events on torch's current stream (the stream libzq launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.spans = {}
+
+    def span(self, name):
+        ev0 = self.torch.cuda.Event(enable_timing=True)
+        ev1 = self.torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        timer = self
+
+        class _S:
+            def __enter__(self_):
+                return self_
+
+            def __exit__(self_, *a):
+                ev1.record()
+                timer.spans.setdefault(name, []).append((ev0, ev1))
+        return _S()
+
+    def ms(self, name):
+        return [a.elapsed_time(b) for a, b in self.spans.get(name, [])]
+
+
+def main():
+    args = parse()
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof)
+        return
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU exchange (RCCL all-to-all over xGMI) is not part of it.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from weight_communication_zero_amd import zq
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------- main workload --
+    tensors = synth.llama_7p5b()
+    M = synth.total(tensors)
+    B = 128
+    P1, P2 = 8, 4
+    n1, n2 = M // P1, M // (P1 * P2)
+    beta = 0.9
+    log(f"allocating {M} fp32 gradient + EF + codes on {torch.cuda.get_device_name(0)}")
+    g = torch.empty(M, dtype=torch.float32, device=dev)
+    t0 = time.time()
+    synth.fill_model(g, tensors, std=1e-3, seed=synth.seed_for("llama7p5b", "grad"),
+                     heavy_tails=True)
+    ef = torch.zeros(M, dtype=torch.float32, device=dev)
+    codes = torch.empty(zq.int4_code_bytes(M), dtype=torch.uint8, device=dev)
+    scales = torch.empty(zq.num_blocks(M, B), dtype=torch.float32, device=dev)
+    rq_codes = torch.empty(zq.int4_code_bytes(n1), dtype=torch.uint8, device=dev)
+    rq_scales = torch.empty(zq.num_blocks(n1, B), dtype=torch.float32, device=dev)
+    out2 = torch.empty(n2, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s")
+
+    cb1, sb1 = n1 // 2, n1 // B
+    cb2, sb2 = n2 // 2, n2 // B
+    chunks_c = [codes[j * cb1:(j + 1) * cb1] for j in range(P1)]
+    chunks_s = [scales[j * sb1:(j + 1) * sb1] for j in range(P1)]
+    sub_c = [rq_codes[j * cb2:(j + 1) * cb2] for j in range(P2)]
+    sub_s = [rq_scales[j * sb2:(j + 1) * sb2] for j in range(P2)]
+
+    def step(timer=None):
+        def run(name, fn):
+            if timer is None:
+                fn()
+            else:
+                with timer.span(name):
+                    fn()
+        run("efq", lambda: zq.zq_quantize_ef_int4(g, ef, B, beta, 1.0, codes, scales))
+        run("dr_rq", lambda: zq.zq_dequant_reduce(chunks_c, chunks_s, n1, B, 1.0, out=None,
+                                                  rq_codes=rq_codes, rq_scales=rq_scales))
+        run("dr", lambda: zq.zq_dequant_reduce(sub_c, sub_s, n2, B, 1.0 / 32, out=out2))
+
+    bytes_efq = efq_bytes(M, B, 4)
+    bytes_dr_rq = dr_bytes(n1, B, P1, out=False, rq=True)
+    bytes_dr = dr_bytes(n2, B, P2, out=True)
+    bytes_step = bytes_efq + bytes_dr_rq + bytes_dr
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timer = EventTimer(torch)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        step(timer)
+    t_end.record()
+    torch.cuda.synchronize()
+    step_ms = t_start.elapsed_time(t_end) / max(args.steps, 1)
+    k_ms = {k: float(np.mean(timer.ms(k))) for k in ("efq", "dr_rq", "dr")}
+    value = bytes_step / (step_ms * 1e-3) / 1e9
+    log(f"step {step_ms:.3f} ms, {value:.1f} GB/s; kernels (ms) {k_ms}")
+
+    if args.calib_copy:
+        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    efq_gbs = bytes_efq / (k_ms["efq"] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(efq_gbs, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(efq_gbs / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic("efq_fp32_b128", bytes_efq),
+                "kernel": "efq_kernel<fp32, ef, B=128>", "bytes_per_launch": bytes_efq,
+                "avg_launch_ms": round(k_ms["efq"], 4)}
+
+    rows = {
+        "efq_fp32_b128_7.5B": row(bytes_efq, k_ms["efq"], M),
+        "dequant_reduce_requant_p8_b128_7.5B": row(bytes_dr_rq, k_ms["dr_rq"], n1),
+        "dequant_reduce_p4_b128_7.5B": row(bytes_dr, k_ms["dr"], n2),
+    }
+
+    # ---------------------------------------------------- CPU baseline --
+    cpu = None
+    if not args.no_cpu:
+        S = args.cpu_sample_elems
+        g_host = g[:S].cpu().numpy()
+        cpu = cpu_baseline(g_host, B, beta, P1, P2)
+        del g_host
+        log(f"cpu baseline {cpu}")
+
+    del g, ef, codes, scales, rq_codes, rq_scales, out2, chunks_c, chunks_s, sub_c, sub_s
+    torch.cuda.empty_cache()
+
+    if not args.no_rows:
+        rows.update(extra_rows(torch, zq, synth, dev, log))
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded normal gradients, Student-t heavy-tailed tensors; no dataset)",
+        "config": {
+            "workload": "two-level qgZ + LoCo on one GPU's share of a ~7.5B Llama-2-style fp32 "
+                        "gradient: EF int4 quantize (block 128, beta 0.9) -> 8-way "
+                        "dequant-reduce-requant -> 4-way dequant-reduce (alpha 1/32)",
+            "elements": M, "block": B, "peers_intra": P1, "peers_inter": P2,
+            "bytes_per_step": bytes_step, "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
+            "gpu": torch.cuda.get_device_name(0),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def row(nbytes, ms, elems):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "Gelem/s": round(elems / (ms * 1e-3) / 1e9, 3), "bytes": nbytes}
+
+
+def measured_traffic(kernel_tag, algorithmic_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this kernel, if its recorded source hash matches the current kernel
+    source; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_counters.md")
+    src = os.path.join(ROOT, "weight_communication_zero_amd", "csrc")
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(src)):
+        with open(os.path.join(src, f), "rb") as fh:
+            h.update(fh.read())
+    text = open(path).read()
+    m_hash = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != h.hexdigest():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(g_host, B, beta, P1, P2):
+    """The CPU oracle (single-threaded C, as written: never tuned) on a
+    self-contained sample of the same path: EF quantize of the first S
+    gradient elements, 8-way reduce-requant of its 8 chunks, 4-way reduce of
+    the 4 sub-chunks."""
+    import numpy as np
+
+    import oracle as O
+    S = g_host.size
+    ef = np.zeros(S, np.float32)
+    t0 = time.perf_counter()
+    c, s = O.quantize_ef_int4(g_host, ef, B, beta, 1.0)
+    t1 = time.perf_counter()
+    n1 = S // P1
+    _, rc, rs = O.dequant_reduce([c[j * n1 // 2:(j + 1) * n1 // 2] for j in range(P1)],
+                                 [s[j * n1 // B:(j + 1) * n1 // B] for j in range(P1)], n1, B,
+                                 1.0, want_out=False, requant=True)
+    t2 = time.perf_counter()
+    n2 = n1 // P2
+    O.dequant_reduce([rc[j * n2 // 2:(j + 1) * n2 // 2] for j in range(P2)],
+                     [rs[j * n2 // B:(j + 1) * n2 // B] for j in range(P2)], n2, B, 1.0 / 32)
+    t3 = time.perf_counter()
+    nbytes = efq_bytes(S, B, 4) + dr_bytes(n1, B, P1, out=False, rq=True) + dr_bytes(n2, B, P2)
+    return {"value": round(nbytes / (t3 - t0) / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"first {S} elements of the same gradient: EF quantize + 8-way "
+                      f"reduce-requant of its {n1}-element chunks + 4-way reduce of {n2}",
+            "seconds": round(t3 - t0, 2),
+            "split_s": {"efq": round(t1 - t0, 2), "dr_rq": round(t2 - t1, 2),
+                        "dr": round(t3 - t2, 2)},
+            "host": platform.processor() or platform.machine(), "host_nproc": os.cpu_count()}
+
+
+def summarize_rocprof(d):
+    """Summaries of rocprofv3 CSVs: kernel_stats (average duration per
+    kernel) and counter_collection (per-kernel mean of each counter)."""
+    import csv
+    import glob
+    from collections import defaultdict
+    for path in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+        print(f"# kernel stats: {os.path.relpath(path, d)}")
+        print(f"{'calls':>6} {'avg_ms':>10} {'min_ms':>10} {'max_ms':>10} {'pct':>6}  kernel")
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                print(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e6:10.4f} "
+                      f"{float(r['MinNs']) / 1e6:10.4f} {float(r['MaxNs']) / 1e6:10.4f} "
+                      f"{float(r['Percentage']):6.2f}  {r['Name'][:140]}")
+    for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        print(f"# counters: {os.path.relpath(path, d)}  (value per dispatch, mean over dispatches)")
+        acc = defaultdict(list)
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                acc[(r["Kernel_Name"][:140], r["Counter_Name"], r.get("Grid_Size", ""))].append(
+                    float(r["Counter_Value"]))
+        print(f"{'dispatches':>10} {'counter':>12} {'mean':>16} {'grid':>12}  kernel")
+        for (k, c, gs), v in sorted(acc.items(), key=lambda kv: -sum(kv[1]) / len(kv[1])):
+            print(f"{len(v):10d} {c:>12} {sum(v) / len(v):16.1f} {gs:>12}  {k}")
+
+
+def timed(torch, fn, reps, warm=2):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    import numpy as np
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+
+def extra_rows(torch, zq, synth, dev, log):
+    """The other rows of the path, each on its own workload."""
+    rows = {}
+    # qwZ: bf16 weights of the ~0.85B model, block 2048
+    t3 = synth.llama_0p85b()
+    n = synth.total(t3)
+    w = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    synth.fill_model(w, t3, std=0.02, seed=synth.seed_for("llama0p85b", "weights"))
+    c8 = torch.empty(n, dtype=torch.int8, device=dev)
+    s8 = torch.empty(zq.num_blocks(n, 2048), dtype=torch.float32, device=dev)
+    wd = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    ms = timed(torch, lambda: zq.zq_quant_int8(w, 2048, c8, s8), 20)
+    rows["quant_int8_bf16_b2048_0.85B"] = row(n * 3 + 4 * s8.numel(), ms, n)
+    ms = timed(torch, lambda: zq.zq_dequant_int8(c8, s8, 2048, wd), 20)
+    rows["dequant_int8_bf16_b2048_0.85B"] = row(n * 3 + 4 * s8.numel(), ms, n)
+    log("int8 rows", rows["quant_int8_bf16_b2048_0.85B"], rows["dequant_int8_bf16_b2048_0.85B"])
+    del w, c8, s8, wd
+
+    # qgZ + LoCo on the ~0.85B fp32 gradient: EF quantize B=128 + 8-way reduce
+    gq = torch.empty(n, dtype=torch.float32, device=dev)
+    synth.fill_model(gq, t3, std=1e-3, seed=synth.seed_for("llama0p85b", "grad"), heavy_tails=True)
+    efq_ = torch.zeros(n, dtype=torch.float32, device=dev)
+    cq = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+    sq = torch.empty(n // 128, dtype=torch.float32, device=dev)
+    outq = torch.empty(n // 8, dtype=torch.float32, device=dev)
+    ms = timed(torch, lambda: zq.zq_quantize_ef_int4(gq, efq_, 128, 0.9, 1.0, cq, sq), 10)
+    rows["efq_fp32_b128_0.85B"] = row(efq_bytes(n, 128, 4), ms, n)
+    nc = n // 8
+    cc = [cq[j * nc // 2:(j + 1) * nc // 2] for j in range(8)]
+    ss = [sq[j * nc // 128:(j + 1) * nc // 128] for j in range(8)]
+    ms = timed(torch, lambda: zq.zq_dequant_reduce(cc, ss, nc, 128, 0.125, out=outq), 20)
+    rows["dequant_reduce_p8_b128_0.85B"] = row(dr_bytes(nc, 128, 8), ms, nc)
+    log("0.85B qgZ rows", rows["efq_fp32_b128_0.85B"], rows["dequant_reduce_p8_b128_0.85B"])
+    del gq, efq_, cq, sq, outq, cc, ss
+
+    # llm.c ZeRO-2: SR accumulation of GPT-2 124M bf16 grads, full buffer and rank-3 shard
+    t2 = synth.gpt2_124m()
+    n = synth.total(t2)
+    dst = torch.zeros(n, dtype=torch.bfloat16, device=dev)
+    src = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    synth.fill_model(src, t2, std=1e-4, seed=synth.seed_for("gpt2", "grad", mb=0))
+    ms = timed(torch, lambda: zq.zq_sr_accumulate(dst, src, 0, 0), 20)
+    rows["sr_accumulate_bf16_gpt2_124M_full"] = row(6 * n, ms, n)
+    shard = n // 8
+    off = 3 * shard
+    dsh = torch.zeros(shard, dtype=torch.bfloat16, device=dev)
+    ssh = src[off:off + shard]
+    ms = timed(torch, lambda: zq.zq_sr_accumulate(dsh, ssh, 0, off), 50)
+    rows["sr_accumulate_bf16_gpt2_rank3_shard"] = dict(row(6 * shard, ms, shard),
+                                                       note="cache-resident (93 MB)")
+    log("SR rows", rows["sr_accumulate_bf16_gpt2_124M_full"])
+    del dst, src, dsh, ssh
+
+    # 4 simulated ranks, bf16 2^20 each, block 256 (cache-resident, launch-bound)
+    n = 4 << 20
+    g4 = synth.grad_with_outliers(n, 1e-3, 0.01, 50.0, synth.seed_for("c1", "grad"),
+                                  torch.bfloat16, device=dev)
+    e4 = torch.zeros(n, dtype=torch.float32, device=dev)
+    c4 = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+    s4 = torch.empty(n // 256, dtype=torch.float32, device=dev)
+    ms = timed(torch, lambda: zq.zq_quantize_ef_int4(g4, e4, 256, 1.0, 1.0, c4, s4), 50)
+    rows["efq_bf16_b256_4x2^20"] = dict(row(efq_bytes(n, 256, 2), ms, n),
+                                       note="cache-resident (44 MB)")
+    torch.cuda.empty_cache()
+    return rows
+
+
+if __name__ == "__main__":
+    main()

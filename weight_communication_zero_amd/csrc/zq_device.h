@@ -14,9 +14,36 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
+// Streaming memory hints: data read or written once goes through the cache
+// hierarchy with the nontemporal bit (global_load/store ... nt), so it does
+// not evict what other waves still need.  Build-time switches for tuning.
+#ifndef ZQ_NT_LOAD
+#define ZQ_NT_LOAD 1
+#endif
+#ifndef ZQ_NT_STORE
+#define ZQ_NT_STORE 1
+#endif
+
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T* p) {
+    if constexpr (ZQ_NT_LOAD)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+
+template <typename T>
+__device__ __forceinline__ void st_stream(T v, T* p) {
+    if constexpr (ZQ_NT_STORE)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
+}
+
 constexpr int kWave = 64;
-constexpr int kBlockThreads = 256;  // 4 waves per workgroup
-constexpr int kWavesPerWG = kBlockThreads / kWave;
+// Workgroups hold 1 to 4 waves (chosen per kernel at launch); kernels are
+// compiled for the largest.
+constexpr int kBlockThreads = 256;
 
 __device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ __forceinline__ float bitsf(uint32_t u) { return __builtin_bit_cast(float, u); }
@@ -107,17 +134,24 @@ __device__ __forceinline__ float code_fast(float x, const BlockScale& b, bool& r
 }
 
 // Rare path: recompute with the IEEE quotient where the fast code is unsafe.
+// The clamp to [-qmax, qmax] is only reachable here: with s = fl(a / qmax)
+// every |x| <= a gives |x / s| <= qmax (1 + 2^-24) and |x * rcp(s)| <=
+// qmax (1 + 2^-22), both below qmax + 1/2, so outside a subnormal-scale block
+// no code can leave the range.
 template <int QMAX>
 __device__ __forceinline__ float code_fix(float x, const BlockScale& b, float k) {
     const float y = x * b.inv;
-    if (b.exact || __builtin_fabsf(y - rintf(y)) > tie_band<QMAX>())
+    if (b.exact || __builtin_fabsf(y - rintf(y)) > tie_band<QMAX>()) {
         k = rintf(x / b.s);
+        k = __builtin_fminf(__builtin_fmaxf(k, -(float)QMAX), (float)QMAX);
+    }
     return k;
 }
 
+// Integer code of a (fast or fixed) rounded quotient.
 template <int QMAX>
 __device__ __forceinline__ int code_clamp(float k) {
-    return (int)__builtin_fminf(__builtin_fmaxf(k, -(float)QMAX), (float)QMAX);
+    return (int)k;
 }
 
 // Residual of the error-feedback quantizer and the new EF value:
@@ -178,11 +212,12 @@ __device__ __forceinline__ uint32_t sr_bf16(float x, uint32_t r16) {
 
 // ---------------------------------------------------------------------------
 // Launch geometry shared by the streaming kernels: a wave owns whole tiles
-// (a multiple of the quantization block), walking them with a grid stride.
+// (a multiple of the quantization block), walking them with a grid stride
+// when the grid is capped.
 __device__ __forceinline__ size_t wave_id() {
-    return (size_t)blockIdx.x * kWavesPerWG + (threadIdx.x >> 6);
+    return (size_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
 }
-__device__ __forceinline__ size_t wave_count() { return (size_t)gridDim.x * kWavesPerWG; }
+__device__ __forceinline__ size_t wave_count() { return (size_t)gridDim.x * (blockDim.x >> 6); }
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
 }  // namespace zq

@@ -70,7 +70,7 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
             for (int u = 0; u < G::U; ++u) {
                 const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * 8;
                 if constexpr (!MASK) {
-                    cw[q][u] = __builtin_nontemporal_load((const uint32_t*)(p.codes[q] + i0 / 2));
+                    cw[q][u] = ld_stream((const uint32_t*)(p.codes[q] + i0 / 2));
                     sc[q][u] = p.scales[q][i0 / B];
                 } else {
                     cw[q][u] = load_code_word_masked(p.codes[q], i0 / 2, nbytes);
@@ -79,13 +79,18 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
             }
         }
     }
+#pragma unroll
+    for (int u = 0; u < G::U; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            e2[u][j] = 0.0f;
     if (RQEF) {
 #pragma unroll
         for (int u = 0; u < G::U; ++u) {
             const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * 8;
             if constexpr (!MASK) {
-                f4 a = __builtin_nontemporal_load((const f4*)(p.rq_ef + i0));
-                f4 b = __builtin_nontemporal_load((const f4*)(p.rq_ef + i0 + 4));
+                f4 a = ld_stream((const f4*)(p.rq_ef + i0));
+                f4 b = ld_stream((const f4*)(p.rq_ef + i0 + 4));
                 e2[u][0] = a.x; e2[u][1] = a.y; e2[u][2] = a.z; e2[u][3] = a.w;
                 e2[u][4] = b.x; e2[u][5] = b.y; e2[u][6] = b.z; e2[u][7] = b.w;
             } else {
@@ -96,19 +101,31 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
         }
     }
 
-    // Dequantize and reduce, ascending peer order.
+    // Dequantize and reduce, ascending peer order.  Peers are the outer loop
+    // so the runtime test q < P is one uniform branch per peer, not a select
+    // per element; alpha = 1 is skipped (multiplying by one is the identity).
     float R[G::U][8];
 #pragma unroll
-    for (int u = 0; u < G::U; ++u) {
+    for (int u = 0; u < G::U; ++u)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float S = nib(cw[0][u], j) * sc[0][u];
+        for (int j = 0; j < 8; ++j)
+            R[u][j] = nib(cw[0][u], j) * sc[0][u];
 #pragma unroll
-            for (int q = 1; q < PMAX; ++q)
-                if (q < (int)p.P)
-                    S = S + nib(cw[q][u], j) * sc[q][u];
-            R[u][j] = p.alpha * S;
+    for (int q = 1; q < PMAX; ++q) {
+        if (q < (int)p.P) {
+#pragma unroll
+            for (int u = 0; u < G::U; ++u)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    R[u][j] = R[u][j] + nib(cw[q][u], j) * sc[q][u];
         }
+    }
+    if (p.alpha != 1.0f) {
+#pragma unroll
+        for (int u = 0; u < G::U; ++u)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                R[u][j] = p.alpha * R[u][j];
     }
 
     if constexpr (OUT) {
@@ -118,8 +135,8 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
             if constexpr (!MASK) {
                 f4 a = {R[u][0], R[u][1], R[u][2], R[u][3]};
                 f4 b = {R[u][4], R[u][5], R[u][6], R[u][7]};
-                __builtin_nontemporal_store(a, (f4*)(p.out + i0));
-                __builtin_nontemporal_store(b, (f4*)(p.out + i0 + 4));
+                st_stream(a, (f4*)(p.out + i0));
+                st_stream(b, (f4*)(p.out + i0 + 4));
             } else {
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
@@ -130,12 +147,15 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
     }
 
     if constexpr (RQ) {
+        // Without a requant EF buffer e2 is zero: R + 0 differs from R only
+        // for R = -0, which quantizes and scales exactly like +0, so one add
+        // serves both cases without a per-element select.
         float c[G::U][8];
 #pragma unroll
         for (int u = 0; u < G::U; ++u)
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                c[u][j] = RQEF ? R[u][j] + e2[u][j] : R[u][j];
+                c[u][j] = R[u][j] + e2[u][j];
         // Beyond n the value must not enter the block max.
         if constexpr (MASK) {
 #pragma unroll
@@ -215,12 +235,12 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
                     e2[u][j] = ef_update(c[u][j], k, s.s, e2[u][j], p.rq_beta_e, p.rq_beta_r);
             }
             if constexpr (!MASK) {
-                __builtin_nontemporal_store(packed, (uint32_t*)(p.rq_codes + i0 / 2));
+                st_stream(packed, (uint32_t*)(p.rq_codes + i0 / 2));
                 if (RQEF) {
                     f4 a = {e2[u][0], e2[u][1], e2[u][2], e2[u][3]};
                     f4 b = {e2[u][4], e2[u][5], e2[u][6], e2[u][7]};
-                    __builtin_nontemporal_store(a, (f4*)(p.rq_ef + i0));
-                    __builtin_nontemporal_store(b, (f4*)(p.rq_ef + i0 + 4));
+                    st_stream(a, (f4*)(p.rq_ef + i0));
+                    st_stream(b, (f4*)(p.rq_ef + i0 + 4));
                 }
             } else {
 #pragma unroll
@@ -239,29 +259,35 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
 }
 
 // PMAX: the kernel serves every P <= PMAX; only PMAX pointer pairs stay
-// live, so the common P = 4 / 8 cases keep their pointers in SGPRs.
-template <int B, int PMAX, bool OUT, bool RQ>
+// live, so the common P = 4 / 8 cases keep their pointers in SGPRs.  Full
+// tiles only; the ragged last tile is a second one-wave launch (MASK).
+template <int B, int PMAX, bool OUT, bool RQ, bool MASK>
 __global__ __launch_bounds__(kBlockThreads) void dr_kernel(DrParams p) {
     using G = DrGeom<B>;
-    const size_t ntiles = (p.n + G::TILE - 1) / G::TILE;
-    const size_t nfull = p.n / G::TILE;
-    for (size_t t = wave_id(); t < ntiles; t += wave_count()) {
-        if (t < nfull)
+    if constexpr (MASK) {
+        dr_tile<B, PMAX, OUT, RQ, true>(p, p.n / G::TILE);
+    } else {
+        const size_t nfull = p.n / G::TILE;
+        for (size_t t = wave_id(); t < nfull; t += wave_count())
             dr_tile<B, PMAX, OUT, RQ, false>(p, t);
-        else
-            dr_tile<B, PMAX, OUT, RQ, true>(p, t);
     }
 }
 
 template <int B, int PMAX, bool OUT, bool RQ>
 hipError_t launch_b(const DrParams& p, hipStream_t stream) {
     using G = DrGeom<B>;
-    const size_t tiles = (p.n + G::TILE - 1) / G::TILE;
+    const size_t nfull = p.n / G::TILE;
     DrParams arg = p;
     void* args[] = {(void*)&arg};
-    return hipLaunchKernel((const void*)&dr_kernel<B, PMAX, OUT, RQ>,
-                           dim3(grid_for_tiles(tiles, kWavesPerWG)), dim3(kBlockThreads), args, 0,
-                           stream);
+    constexpr Geometry geom = RQ ? kGeomReduceRequant : kGeomReduce;
+    hipError_t e = hipSuccess;
+    if (nfull)
+        e = hipLaunchKernel((const void*)&dr_kernel<B, PMAX, OUT, RQ, false>,
+                            grid_for_tiles(nfull, geom), dim3(geom.threads), args, 0, stream);
+    if (e == hipSuccess && p.n % G::TILE)
+        e = hipLaunchKernel((const void*)&dr_kernel<B, PMAX, OUT, RQ, true>, dim3(1), dim3(kWave),
+                            args, 0, stream);
+    return e;
 }
 
 template <int B, int PMAX>

@@ -17,6 +17,10 @@
 #include "zq_device.h"
 #include "zq_launch.h"
 
+#ifndef ZQ_EFQ_U
+#define ZQ_EFQ_U 4  // sub-vectors of 256 elements per wave tile
+#endif
+
 namespace zq {
 namespace {
 
@@ -26,7 +30,7 @@ struct EfqGeom {
     static constexpr int SUB = kWave * VEC;
     static constexpr int LPB = B <= SUB ? B / VEC : kWave;
     static constexpr int SPB = B <= SUB ? 1 : B / SUB;
-    static constexpr int U = SPB > 4 ? SPB : 4;
+    static constexpr int U = SPB > ZQ_EFQ_U ? SPB : ZQ_EFQ_U;
     static constexpr int TILE = SUB * U;
     static constexpr int BPT = TILE / B;
 };
@@ -49,20 +53,20 @@ __device__ __forceinline__ void efq_tile(const void* __restrict__ gv, float* __r
         float gv4[4];
         if constexpr (!MASK) {
             if constexpr (BF16) {
-                u2 w = __builtin_nontemporal_load((const u2*)((const uint16_t*)gv + i0));
+                u2 w = ld_stream((const u2*)((const uint16_t*)gv + i0));
                 gv4[0] = bf16lo(w.x);
                 gv4[1] = bf16hi(w.x);
                 gv4[2] = bf16lo(w.y);
                 gv4[3] = bf16hi(w.y);
             } else {
-                f4 w = __builtin_nontemporal_load((const f4*)((const float*)gv + i0));
+                f4 w = ld_stream((const f4*)((const float*)gv + i0));
                 gv4[0] = w.x;
                 gv4[1] = w.y;
                 gv4[2] = w.z;
                 gv4[3] = w.w;
             }
             if constexpr (EF) {
-                f4 v = __builtin_nontemporal_load((const f4*)(ef + i0));
+                f4 v = ld_stream((const f4*)(ef + i0));
                 e[u][0] = v.x;
                 e[u][1] = v.y;
                 e[u][2] = v.z;
@@ -157,10 +161,10 @@ __device__ __forceinline__ void efq_tile(const void* __restrict__ gv, float* __r
                 e[u][j] = ef_update(c[u][j], k, sc.s, e[u][j], beta_e, beta_r);
         }
         if constexpr (!MASK) {
-            __builtin_nontemporal_store((uint16_t)packed, (uint16_t*)(codes + i0 / 2));
+            st_stream((uint16_t)packed, (uint16_t*)(codes + i0 / 2));
             if constexpr (EF) {
                 f4 v = {e[u][0], e[u][1], e[u][2], e[u][3]};
-                __builtin_nontemporal_store(v, (f4*)(ef + i0));
+                st_stream(v, (f4*)(ef + i0));
             }
         } else {
             if (i0 < n)
@@ -177,20 +181,21 @@ __device__ __forceinline__ void efq_tile(const void* __restrict__ gv, float* __r
     }
 }
 
-template <bool BF16, bool EF, int B>
+// Full tiles only (no bounds checks in the hot loop); the ragged last tile,
+// if any, is a second one-wave launch of the masked variant.
+template <bool BF16, bool EF, int B, bool MASK>
 __global__ __launch_bounds__(kBlockThreads) void efq_kernel(const void* __restrict__ g,
                                                             float* __restrict__ ef, size_t n,
                                                             float beta_e, float beta_r,
                                                             uint8_t* __restrict__ codes,
                                                             float* __restrict__ scales) {
     using G = EfqGeom<B>;
-    const size_t ntiles = (n + G::TILE - 1) / G::TILE;
-    const size_t nfull = n / G::TILE;
-    for (size_t t = wave_id(); t < ntiles; t += wave_count()) {
-        if (t < nfull)
+    if constexpr (MASK) {
+        efq_tile<BF16, EF, B, true>(g, ef, n, beta_e, beta_r, codes, scales, n / G::TILE);
+    } else {
+        const size_t nfull = n / G::TILE;
+        for (size_t t = wave_id(); t < nfull; t += wave_count())
             efq_tile<BF16, EF, B, false>(g, ef, n, beta_e, beta_r, codes, scales, t);
-        else
-            efq_tile<BF16, EF, B, true>(g, ef, n, beta_e, beta_r, codes, scales, t);
     }
 }
 
@@ -198,12 +203,18 @@ template <bool BF16, bool EF, int B>
 hipError_t launch_b(const void* g, float* ef, size_t n, float beta_e, float beta_r,
                     uint8_t* codes, float* scales, hipStream_t stream) {
     using G = EfqGeom<B>;
-    const size_t tiles = (n + G::TILE - 1) / G::TILE;
+    const size_t nfull = n / G::TILE;
     void* args[] = {(void*)&g, (void*)&ef, (void*)&n, (void*)&beta_e, (void*)&beta_r,
                     (void*)&codes, (void*)&scales};
-    return hipLaunchKernel((const void*)&efq_kernel<BF16, EF, B>,
-                           dim3(grid_for_tiles(tiles, kWavesPerWG)), dim3(kBlockThreads), args, 0,
-                           stream);
+    hipError_t e = hipSuccess;
+    if (nfull)
+        e = hipLaunchKernel((const void*)&efq_kernel<BF16, EF, B, false>,
+                            grid_for_tiles(nfull, kGeomStream), dim3(kGeomStream.threads), args, 0,
+                            stream);
+    if (e == hipSuccess && n % G::TILE)
+        e = hipLaunchKernel((const void*)&efq_kernel<BF16, EF, B, true>, dim3(1), dim3(kWave),
+                            args, 0, stream);
+    return e;
 }
 
 template <bool BF16, bool EF>

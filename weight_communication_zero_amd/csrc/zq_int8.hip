@@ -41,14 +41,14 @@ __device__ __forceinline__ void q8_tile(const void* __restrict__ wv, size_t n,
         const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * 8;
         if constexpr (!MASK) {
             if constexpr (BF16) {
-                u4 w = __builtin_nontemporal_load((const u4*)((const uint16_t*)wv + i0));
+                u4 w = ld_stream((const u4*)((const uint16_t*)wv + i0));
                 x[u][0] = bf16lo(w.x); x[u][1] = bf16hi(w.x);
                 x[u][2] = bf16lo(w.y); x[u][3] = bf16hi(w.y);
                 x[u][4] = bf16lo(w.z); x[u][5] = bf16hi(w.z);
                 x[u][6] = bf16lo(w.w); x[u][7] = bf16hi(w.w);
             } else {
-                f4 a = __builtin_nontemporal_load((const f4*)((const float*)wv + i0));
-                f4 b = __builtin_nontemporal_load((const f4*)((const float*)wv + i0 + 4));
+                f4 a = ld_stream((const f4*)((const float*)wv + i0));
+                f4 b = ld_stream((const f4*)((const float*)wv + i0 + 4));
                 x[u][0] = a.x; x[u][1] = a.y; x[u][2] = a.z; x[u][3] = a.w;
                 x[u][4] = b.x; x[u][5] = b.y; x[u][6] = b.z; x[u][7] = b.w;
             }
@@ -133,7 +133,7 @@ __device__ __forceinline__ void q8_tile(const void* __restrict__ wv, size_t n,
         }
         if constexpr (!MASK) {
             u2 v = {lo, hi};
-            __builtin_nontemporal_store(v, (u2*)(codes + i0));
+            st_stream(v, (u2*)(codes + i0));
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j)
@@ -143,18 +143,17 @@ __device__ __forceinline__ void q8_tile(const void* __restrict__ wv, size_t n,
     }
 }
 
-template <bool BF16, int B>
+template <bool BF16, int B, bool MASK>
 __global__ __launch_bounds__(kBlockThreads) void q8_kernel(const void* __restrict__ w, size_t n,
                                                            int8_t* __restrict__ codes,
                                                            float* __restrict__ scales) {
     using G = Q8Geom<B>;
-    const size_t ntiles = (n + G::TILE - 1) / G::TILE;
-    const size_t nfull = n / G::TILE;
-    for (size_t t = wave_id(); t < ntiles; t += wave_count()) {
-        if (t < nfull)
+    if constexpr (MASK) {
+        q8_tile<BF16, B, true>(w, n, codes, scales, n / G::TILE);
+    } else {
+        const size_t nfull = n / G::TILE;
+        for (size_t t = wave_id(); t < nfull; t += wave_count())
             q8_tile<BF16, B, false>(w, n, codes, scales, t);
-        else
-            q8_tile<BF16, B, true>(w, n, codes, scales, t);
     }
 }
 
@@ -176,7 +175,7 @@ __device__ __forceinline__ void dq8_tile(const int8_t* __restrict__ codes,
     for (int u = 0; u < kDqU; ++u) {
         const size_t i0 = base + (size_t)u * kDqSub + (size_t)lane * 8;
         if constexpr (!MASK) {
-            cw[u] = __builtin_nontemporal_load((const u2*)(codes + i0));
+            cw[u] = ld_stream((const u2*)(codes + i0));
             s[u] = scales[i0 >> log2b];
         } else {
             uint32_t lo = 0, hi = 0;
@@ -206,7 +205,7 @@ __device__ __forceinline__ void dq8_tile(const int8_t* __restrict__ codes,
             if constexpr (!MASK) {
                 u4 o = {pack_bf16_rne(v[0], v[1]), pack_bf16_rne(v[2], v[3]),
                         pack_bf16_rne(v[4], v[5]), pack_bf16_rne(v[6], v[7])};
-                __builtin_nontemporal_store(o, (u4*)((uint16_t*)out + i0));
+                st_stream(o, (u4*)((uint16_t*)out + i0));
             } else {
 #pragma unroll
                 for (int j = 0; j < 8; j += 2) {
@@ -221,8 +220,8 @@ __device__ __forceinline__ void dq8_tile(const int8_t* __restrict__ codes,
             if constexpr (!MASK) {
                 f4 a = {v[0], v[1], v[2], v[3]};
                 f4 b = {v[4], v[5], v[6], v[7]};
-                __builtin_nontemporal_store(a, (f4*)((float*)out + i0));
-                __builtin_nontemporal_store(b, (f4*)((float*)out + i0 + 4));
+                st_stream(a, (f4*)((float*)out + i0));
+                st_stream(b, (f4*)((float*)out + i0 + 4));
             } else {
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
@@ -233,29 +232,34 @@ __device__ __forceinline__ void dq8_tile(const int8_t* __restrict__ codes,
     }
 }
 
-template <bool BF16OUT>
+template <bool BF16OUT, bool MASK>
 __global__ __launch_bounds__(kBlockThreads) void dq8_kernel(const int8_t* __restrict__ codes,
                                                             const float* __restrict__ scales,
                                                             size_t n, uint32_t log2b,
                                                             void* __restrict__ out) {
-    const size_t ntiles = (n + kDqTile - 1) / kDqTile;
-    const size_t nfull = n / kDqTile;
-    for (size_t t = wave_id(); t < ntiles; t += wave_count()) {
-        if (t < nfull)
+    if constexpr (MASK) {
+        dq8_tile<BF16OUT, true>(codes, scales, n, log2b, out, n / kDqTile);
+    } else {
+        const size_t nfull = n / kDqTile;
+        for (size_t t = wave_id(); t < nfull; t += wave_count())
             dq8_tile<BF16OUT, false>(codes, scales, n, log2b, out, t);
-        else
-            dq8_tile<BF16OUT, true>(codes, scales, n, log2b, out, t);
     }
 }
 
 template <bool BF16, int B>
 hipError_t launch_q8_b(const void* w, size_t n, int8_t* codes, float* scales, hipStream_t st) {
     using G = Q8Geom<B>;
-    const size_t tiles = (n + G::TILE - 1) / G::TILE;
+    const size_t nfull = n / G::TILE;
     void* args[] = {(void*)&w, (void*)&n, (void*)&codes, (void*)&scales};
-    return hipLaunchKernel((const void*)&q8_kernel<BF16, B>,
-                           dim3(grid_for_tiles(tiles, kWavesPerWG)), dim3(kBlockThreads), args, 0,
-                           st);
+    hipError_t e = hipSuccess;
+    if (nfull)
+        e = hipLaunchKernel((const void*)&q8_kernel<BF16, B, false>,
+                            grid_for_tiles(nfull, kGeomStream), dim3(kGeomStream.threads), args, 0,
+                            st);
+    if (e == hipSuccess && n % G::TILE)
+        e = hipLaunchKernel((const void*)&q8_kernel<BF16, B, true>, dim3(1), dim3(kWave), args, 0,
+                            st);
+    return e;
 }
 
 template <bool BF16>
@@ -287,11 +291,19 @@ hipError_t launch_dequant_int8(const int8_t* codes, const float* scales, size_t 
     uint32_t log2b = 0;
     while ((1u << log2b) < block)
         ++log2b;
-    const size_t tiles = (n + kDqTile - 1) / kDqTile;
+    const size_t nfull = n / kDqTile;
     void* args[] = {(void*)&codes, (void*)&scales, (void*)&n, (void*)&log2b, (void*)&out};
-    const void* fn = out_bf16 ? (const void*)&dq8_kernel<true> : (const void*)&dq8_kernel<false>;
-    return hipLaunchKernel(fn, dim3(grid_for_tiles(tiles, kWavesPerWG)), dim3(kBlockThreads), args,
-                           0, stream);
+    const void* full = out_bf16 ? (const void*)&dq8_kernel<true, false>
+                                : (const void*)&dq8_kernel<false, false>;
+    const void* tail = out_bf16 ? (const void*)&dq8_kernel<true, true>
+                                : (const void*)&dq8_kernel<false, true>;
+    hipError_t e = hipSuccess;
+    if (nfull)
+        e = hipLaunchKernel(full, grid_for_tiles(nfull, kGeomStream), dim3(kGeomStream.threads),
+                            args, 0, stream);
+    if (e == hipSuccess && n % kDqTile)
+        e = hipLaunchKernel(tail, dim3(1), dim3(kWave), args, 0, stream);
+    return e;
 }
 
 }  // namespace zq

@@ -11,19 +11,29 @@ namespace zq {
 
 constexpr uint32_t kMaxPeers = 16;
 
-// Upper bound on workgroups per launch (grid-stride beyond it).  256 CUs
-// times 16 workgroups of 4 waves keeps every SIMD at full occupancy.
-#ifndef ZQ_MAX_WORKGROUPS
-#define ZQ_MAX_WORKGROUPS 4096
-#endif
+// Launch geometry of a streaming kernel: threads per workgroup (64..256)
+// and the most workgroups one launch may have; a larger job walks its tiles
+// with a grid stride.  Measured on MI355X: one-tile-per-wave grids of 1-wave
+// workgroups stream best (the dispatcher keeps every CU fed and a wave never
+// waits on a sibling), except for the ALU-heavy reduce+requant, which runs
+// best persistent (4096 workgroups of 4 waves walking many tiles).
+struct Geometry {
+    uint32_t threads;
+    uint32_t max_wgs;
+};
 
-inline uint32_t grid_for_tiles(size_t tiles, size_t waves_per_wg) {
-    size_t wgs = (tiles + waves_per_wg - 1) / waves_per_wg;
-    if (wgs > ZQ_MAX_WORKGROUPS)
-        wgs = ZQ_MAX_WORKGROUPS;
+constexpr Geometry kGeomStream{64, 1u << 24};       // EF quantize, int8, SR
+constexpr Geometry kGeomReduce{256, 1u << 22};      // dequant-reduce into fp32
+constexpr Geometry kGeomReduceRequant{256, 4096};   // dequant-reduce-requant
+
+inline dim3 grid_for_tiles(size_t tiles, Geometry g) {
+    const size_t per_wg = g.threads / 64;
+    size_t wgs = (tiles + per_wg - 1) / per_wg;
+    if (wgs > g.max_wgs)
+        wgs = g.max_wgs;
     if (wgs == 0)
         wgs = 1;
-    return (uint32_t)wgs;
+    return dim3((uint32_t)wgs);
 }
 
 hipError_t launch_quantize_ef_int4(const void* g, bool g_bf16, float* ef, size_t n, uint32_t block,

@@ -49,8 +49,8 @@ __device__ __forceinline__ void sr_tile(uint16_t* __restrict__ dst, uint16_t* __
     for (int u = 0; u < kSrU; ++u) {
         const size_t i0 = base + (size_t)u * kSrSub + (size_t)lane * 8;
         if constexpr (!MASK) {
-            d[u] = __builtin_nontemporal_load((const u4*)(dst + i0));
-            s[u] = __builtin_nontemporal_load((const u4*)(src + i0));
+            d[u] = ld_stream((const u4*)(dst + i0));
+            s[u] = ld_stream((const u4*)(src + i0));
         } else {
             uint32_t dv[4] = {0, 0, 0, 0}, sv[4] = {0, 0, 0, 0};
 #pragma unroll
@@ -78,9 +78,9 @@ __device__ __forceinline__ void sr_tile(uint16_t* __restrict__ dst, uint16_t* __
             o[h] = sr_bf16(x0, r[2 * h]) | (sr_bf16(x1, r[2 * h + 1]) << 16);
         }
         if constexpr (!MASK) {
-            __builtin_nontemporal_store(u4{o[0], o[1], o[2], o[3]}, (u4*)(dst + i0));
+            st_stream(u4{o[0], o[1], o[2], o[3]}, (u4*)(dst + i0));
             if constexpr (ZERO)
-                __builtin_nontemporal_store(u4{0u, 0u, 0u, 0u}, (u4*)(src + i0));
+                st_stream(u4{0u, 0u, 0u, 0u}, (u4*)(src + i0));
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j)
@@ -93,47 +93,57 @@ __device__ __forceinline__ void sr_tile(uint16_t* __restrict__ dst, uint16_t* __
     }
 }
 
-template <int PHASE, bool ZERO>
+template <int PHASE, bool ZERO, bool MASK>
 __global__ __launch_bounds__(kBlockThreads) void sr_kernel(uint16_t* __restrict__ dst,
                                                            uint16_t* __restrict__ src, size_t n,
                                                            uint32_t k0, uint32_t k1,
                                                            uint64_t cbase8) {
-    const size_t ntiles = (n + kSrTile - 1) / kSrTile;
-    const size_t nfull = n / kSrTile;
-    for (size_t t = wave_id(); t < ntiles; t += wave_count()) {
-        if (t < nfull)
+    if constexpr (MASK) {
+        sr_tile<PHASE, ZERO, true>(dst, src, n, k0, k1, cbase8, n / kSrTile);
+    } else {
+        const size_t nfull = n / kSrTile;
+        for (size_t t = wave_id(); t < nfull; t += wave_count())
             sr_tile<PHASE, ZERO, false>(dst, src, n, k0, k1, cbase8, t);
-        else
-            sr_tile<PHASE, ZERO, true>(dst, src, n, k0, k1, cbase8, t);
     }
 }
 
-template <int PHASE>
+template <int PHASE, bool MASK>
 const void* sr_fn(bool zero) {
-    return zero ? (const void*)&sr_kernel<PHASE, true> : (const void*)&sr_kernel<PHASE, false>;
+    return zero ? (const void*)&sr_kernel<PHASE, true, MASK>
+                : (const void*)&sr_kernel<PHASE, false, MASK>;
+}
+
+template <bool MASK>
+const void* sr_pick(uint64_t counter_base, bool zero) {
+    switch (counter_base & 7u) {
+        case 0: return sr_fn<0, MASK>(zero);
+        case 1: return sr_fn<1, MASK>(zero);
+        case 2: return sr_fn<2, MASK>(zero);
+        case 3: return sr_fn<3, MASK>(zero);
+        case 4: return sr_fn<4, MASK>(zero);
+        case 5: return sr_fn<5, MASK>(zero);
+        case 6: return sr_fn<6, MASK>(zero);
+        default: return sr_fn<7, MASK>(zero);
+    }
 }
 
 }  // namespace
 
 hipError_t launch_sr_accumulate(uint16_t* dst, uint16_t* src, size_t n, uint64_t seed,
                                 uint64_t counter_base, bool zero_src, hipStream_t stream) {
-    const void* fn = nullptr;
-    switch (counter_base & 7u) {
-        case 0: fn = sr_fn<0>(zero_src); break;
-        case 1: fn = sr_fn<1>(zero_src); break;
-        case 2: fn = sr_fn<2>(zero_src); break;
-        case 3: fn = sr_fn<3>(zero_src); break;
-        case 4: fn = sr_fn<4>(zero_src); break;
-        case 5: fn = sr_fn<5>(zero_src); break;
-        case 6: fn = sr_fn<6>(zero_src); break;
-        default: fn = sr_fn<7>(zero_src); break;
-    }
     uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
     uint64_t cbase8 = counter_base >> 3;
-    const size_t tiles = (n + kSrTile - 1) / kSrTile;
+    const size_t nfull = n / kSrTile;
     void* args[] = {(void*)&dst, (void*)&src, (void*)&n, (void*)&k0, (void*)&k1, (void*)&cbase8};
-    return hipLaunchKernel(fn, dim3(grid_for_tiles(tiles, kWavesPerWG)), dim3(kBlockThreads), args,
-                           0, stream);
+    hipError_t e = hipSuccess;
+    if (nfull)
+        e = hipLaunchKernel(sr_pick<false>(counter_base, zero_src),
+                            grid_for_tiles(nfull, kGeomStream), dim3(kGeomStream.threads), args, 0,
+                            stream);
+    if (e == hipSuccess && n % kSrTile)
+        e = hipLaunchKernel(sr_pick<true>(counter_base, zero_src), dim3(1), dim3(kWave), args, 0,
+                            stream);
+    return e;
 }
 
 }  // namespace zq

@@ -16,7 +16,8 @@ import re
 import torch  # loaded first: libzq then binds to the HIP runtime torch uses
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libzq.so")
+# ZQ_LIB selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("ZQ_LIB") or os.path.join(_HERE, "libzq.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "zq.h")
 
 ZQ_FP32, ZQ_BF16 = 0, 1
