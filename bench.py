@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed steps, run a 1 GiB fp32 copy (known HBM bytes) so that "
                          "rocprofv3 memory counters can be scaled")
+    ap.add_argument("--kernels", action="store_true",
+                    help="time every entry point on 2^31-element buffers next to torch copy / add / "
+                         "sum / fill ceilings, print one line and exit (with ZQ_LIB=<build> this "
+                         "compares library builds)")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="print a summary of the rocprofv3 CSV output under DIR and exit")
     return ap.parse_args()
@@ -100,6 +104,9 @@ def main():
     args = parse()
     if args.summarize_rocprof:
         summarize_rocprof(args.summarize_rocprof)
+        return
+    if args.kernels:
+        kernel_table()
         return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -327,6 +334,57 @@ def summarize_rocprof(d):
         print(f"{'dispatches':>10} {'counter':>12} {'mean':>16} {'grid':>12}  kernel")
         for (k, c, gs), v in sorted(acc.items(), key=lambda kv: -sum(kv[1]) / len(kv[1])):
             print(f"{len(v):10d} {c:>12} {sum(v) / len(v):16.1f} {gs:>12}  {k}")
+
+
+def kernel_table():
+    """GB/s of every entry point on 2^31-element buffers (block 128 int4,
+    2048 int8, 8- and 4-way reduce), and of torch's copy / add / sum / fill on
+    the same buffers as the practical ceilings of each traffic mix."""
+    import torch
+
+    from weight_communication_zero_amd import zq
+    dev = torch.device("cuda", 0)
+    n, B = 1 << 31, 128
+    res = {}
+    g = torch.randn(n, device=dev).mul_(1e-3)
+    ef = torch.zeros(n, device=dev)
+    c = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+    s = torch.empty(n // B, device=dev)
+    res["efq"] = efq_bytes(n, B, 4) / timed(torch, lambda: zq.zq_quantize_ef_int4(
+        g, ef, B, 0.9, 1.0, c, s), 10) / 1e6
+    n1 = n // 8
+    cc = [c[j * n1 // 2:(j + 1) * n1 // 2] for j in range(8)]
+    ss = [s[j * n1 // B:(j + 1) * n1 // B] for j in range(8)]
+    rqc = torch.empty(n1 // 2, dtype=torch.uint8, device=dev)
+    rqs = torch.empty(n1 // B, device=dev)
+    out = torch.empty(n1, device=dev)
+    res["dr_rq8"] = dr_bytes(n1, B, 8, out=False, rq=True) / timed(torch, lambda: zq.zq_dequant_reduce(
+        cc, ss, n1, B, 1.0, rq_codes=rqc, rq_scales=rqs), 10) / 1e6
+    res["dr8"] = dr_bytes(n1, B, 8) / timed(torch, lambda: zq.zq_dequant_reduce(
+        cc, ss, n1, B, 0.125, out=out), 10) / 1e6
+    n2 = n1 // 4
+    c2 = [rqc[j * n2 // 2:(j + 1) * n2 // 2] for j in range(4)]
+    s2 = [rqs[j * n2 // B:(j + 1) * n2 // B] for j in range(4)]
+    res["dr4"] = dr_bytes(n2, B, 4) / timed(torch, lambda: zq.zq_dequant_reduce(
+        c2, s2, n2, B, 1 / 32, out=out), 10) / 1e6
+    c3 = torch.empty(n, device=dev)
+    res["torch_copy"] = 8 * n / timed(torch, lambda: c3.copy_(g), 10) / 1e6
+    res["torch_add"] = 12 * n / timed(torch, lambda: torch.add(g, ef, out=c3), 10) / 1e6
+    res["torch_sum"] = 4 * n / timed(torch, lambda: g.sum(), 10) / 1e6
+    res["torch_fill"] = 4 * n / timed(torch, lambda: c3.fill_(1.0), 10) / 1e6
+    del g, ef, c, s, cc, ss, rqc, rqs, out, c2, s2, c3
+    torch.cuda.empty_cache()
+    w = torch.randn(n, device=dev).mul_(0.02).to(torch.bfloat16)
+    c8 = torch.empty(n, dtype=torch.int8, device=dev)
+    s8 = torch.empty(n // 2048, device=dev)
+    wd = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    res["q8"] = (3 * n + 4 * n / 2048) / timed(torch, lambda: zq.zq_quant_int8(w, 2048, c8, s8), 10) / 1e6
+    res["dq8"] = (3 * n + 4 * n / 2048) / timed(torch, lambda: zq.zq_dequant_int8(c8, s8, 2048, wd), 10) / 1e6
+    src = torch.randn(n, device=dev).mul_(1e-4).to(torch.bfloat16)
+    res["sr"] = 6 * n / timed(torch, lambda: zq.zq_sr_accumulate(wd, src, 1, 0), 10) / 1e6
+    res["sr_zero"] = 8 * n / timed(torch, lambda: zq.zq_sr_accumulate(wd, src, 1, 0, zero_src=True), 10) / 1e6
+    lib = os.path.basename(os.environ.get("ZQ_LIB", "libzq.so"))
+    print(f"{lib}  GB/s: " + "  ".join(f"{k} {v:.0f}" for k, v in res.items()), flush=True)
 
 
 def timed(torch, fn, reps, warm=2):

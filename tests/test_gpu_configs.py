@@ -1,0 +1,231 @@
+"""GPU parity at the full sizes of the five workloads, through the same entry
+points and launch configuration the benchmark times.
+
+Every step of the path is block-local, so the oracle can recompute any set of
+blocks on its own: for a sampled output block it recomputes every upstream
+block it depends on (the 8 peer blocks of a first-level reduce, the 4 x 8
+blocks behind a second-level output), starting from the seeded generator's
+inputs and carrying its own error-feedback state across steps -- no oracle
+input ever comes from a GPU output.  Blocks gathered into one array stay
+independent, so each oracle call runs on the concatenation.
+
+Workloads (seeded, synthetic; no dataset):
+  4 ranks x bf16[2^20], N(0, 1e-3) with 1 % outliers x50, block 256, EF beta 1,
+      3 steps, full all-to-all of 2^18-element chunks with alpha 1/4 -- fully
+      compared (small);
+  GPT-2 124M bf16 gradient buffer, 8 micro-batches N(0, 1e-4) accumulated with
+      stochastic rounding (seed = micro-batch), full buffer and rank-3-of-8 shard;
+  ~0.85B Llama-2-style bf16 weights N(0, 0.02), int8 block 2048, quantize + dequantize;
+  ~0.85B fp32 gradient N(0, 1e-3), heavy-tailed tensors, EF int4 block 128,
+      beta 0.9, 10 steps, 8-way reduce alpha 1/8;
+  ~7.5B fp32 gradient, same recipe, 2 steps: EF quantize, 8-way reduce-requant,
+      4-way reduce alpha 1/32.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests.gpu_helpers import assert_bits_equal, to_gpu, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import weight_communication_zero_amd  # noqa: F401
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def Z():
+    from weight_communication_zero_amd import zq
+    return zq
+
+
+def gather_blocks(t: torch.Tensor, blocks: np.ndarray, width: int) -> np.ndarray:
+    """Host copy of the listed blocks (each `width` elements) of a flat tensor."""
+    idx = torch.from_numpy(blocks.astype(np.int64)).to(t.device)
+    return to_host(t.view(-1, width).index_select(0, idx).reshape(-1))
+
+
+def int4_block_bytes(codes: torch.Tensor, blocks: np.ndarray, B: int) -> np.ndarray:
+    return gather_blocks(codes, blocks, B // 2)
+
+
+# ------------------------------------------------------------------ 4 ranks --
+
+def test_four_ranks_bf16_block256_full_compare():
+    P, n, B, steps = 4, 1 << 20, 256, 3
+    nc = n // P
+    ef_o = [np.zeros(n, np.float32) for _ in range(P)]
+    ef_g = [torch.zeros(n, dtype=torch.float32, device="cuda") for _ in range(P)]
+    for step in range(steps):
+        codes_o, scales_o, codes_g, scales_g = [], [], [], []
+        for r in range(P):
+            g = synth.grad_with_outliers(n, 1e-3, 0.01, 50.0, synth.seed_for("c1", "grad", r, step),
+                                         torch.bfloat16)
+            gh = g.view(torch.int16).numpy().view(np.uint16)
+            c_o, s_o = O.quantize_ef_int4(gh, ef_o[r], B, 1.0, 1.0)
+            c = torch.empty(n // 2, dtype=torch.uint8, device="cuda")
+            s = torch.empty(n // B, dtype=torch.float32, device="cuda")
+            Z().zq_quantize_ef_int4(g.cuda(), ef_g[r], B, 1.0, 1.0, c, s)
+            codes_o.append(c_o), scales_o.append(s_o), codes_g.append(c), scales_g.append(s)
+        torch.cuda.synchronize()
+        for r in range(P):
+            assert_bits_equal(to_host(codes_g[r]), codes_o[r], f"step {step} rank {r} codes")
+            assert_bits_equal(to_host(scales_g[r]), scales_o[r], f"step {step} rank {r} scales")
+            assert_bits_equal(to_host(ef_g[r]), ef_o[r], f"step {step} rank {r} ef")
+        for dst in range(P):  # all-to-all: destination dst receives chunk dst of every rank
+            cs_o = [c[dst * nc // 2:(dst + 1) * nc // 2] for c in codes_o]
+            ss_o = [s[dst * nc // B:(dst + 1) * nc // B] for s in scales_o]
+            out_o, _, _ = O.dequant_reduce(cs_o, ss_o, nc, B, 0.25)
+            out = torch.empty(nc, dtype=torch.float32, device="cuda")
+            Z().zq_dequant_reduce([c[dst * nc // 2:(dst + 1) * nc // 2] for c in codes_g],
+                                  [s[dst * nc // B:(dst + 1) * nc // B] for s in scales_g], nc, B,
+                                  0.25, out=out)
+            torch.cuda.synchronize()
+            assert_bits_equal(to_host(out), out_o, f"step {step} reduce at rank {dst}")
+
+
+# --------------------------------------------------------------- GPT-2 SR --
+
+def test_gpt2_sr_accumulation_full_buffer_and_rank3_shard():
+    tensors = synth.gpt2_124m()
+    n = synth.total(tensors)
+    P, rank = 8, 3
+    shard = n // P
+    off = rank * shard
+    rng = np.random.default_rng(2)
+    W = 1024
+    starts = np.unique(np.concatenate([[0, n - W, off, off + shard - W],
+                                       rng.integers(0, n - W, size=60)]))
+    dst = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    dsh = torch.zeros(shard, dtype=torch.bfloat16, device="cuda")
+    src = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    win_o = {int(s0): np.zeros(W, np.uint16) for s0 in starts}
+    for m in range(8):
+        synth.fill_model(src, tensors, std=1e-4, seed=synth.seed_for("gpt2", "grad", mb=m))
+        src_host = {int(s0): to_host(src[s0:s0 + W]).copy() for s0 in starts}
+        Z().zq_sr_accumulate(dst, src, seed=m, counter_base=0)
+        Z().zq_sr_accumulate(dsh, src[off:off + shard], seed=m, counter_base=off)
+        for s0 in starts:
+            O.sr_accumulate(win_o[int(s0)], src_host[int(s0)], seed=m, counter_base=int(s0))
+    torch.cuda.synchronize()
+    assert torch.equal(dst[off:off + shard].view(torch.int16), dsh.view(torch.int16)), \
+        "rank-3 shard differs from the same slice of the full-buffer accumulation"
+    for s0 in starts:
+        assert_bits_equal(to_host(dst[s0:s0 + W]), win_o[int(s0)], f"SR window at {s0}")
+
+
+# ------------------------------------------------------------ qwZ 0.85B --
+
+def test_int8_weights_0p85b_sampled_blocks():
+    tensors = synth.llama_0p85b()
+    n = synth.total(tensors)
+    B = 2048
+    w = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    synth.fill_model(w, tensors, std=0.02, seed=synth.seed_for("llama0p85b", "weights"))
+    codes = torch.empty(n, dtype=torch.int8, device="cuda")
+    scales = torch.empty(n // B, dtype=torch.float32, device="cuda")
+    wd = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    Z().zq_quant_int8(w, B, codes, scales)
+    Z().zq_dequant_int8(codes, scales, B, wd)
+    torch.cuda.synchronize()
+    nb = n // B
+    rng = np.random.default_rng(3)
+    blocks = np.unique(np.concatenate([[0, nb - 1], rng.integers(0, nb, size=254)]))
+    w_h = gather_blocks(w, blocks, B)
+    c_o, s_o = O.quant_int8(w_h, B)
+    assert_bits_equal(gather_blocks(codes, blocks, B).view(np.uint8), c_o.view(np.uint8), "codes")
+    assert_bits_equal(to_host(scales)[blocks], s_o, "scales")
+    assert_bits_equal(gather_blocks(wd, blocks, B), O.dequant_int8(c_o, s_o, B, out_bf16=True),
+                      "dequantized bf16")
+
+
+# ------------------------------------------- qgZ + LoCo: 0.85B and 7.5B --
+
+def run_two_level(tensors, tag, steps, levels, n_sample, seed):
+    """EF quantize of the whole gradient, then level-1 reduce over P1 chunks
+    (with requant when there is a second level), then level-2 reduce over P2
+    sub-chunks; sampled blocks checked at every step."""
+    M = synth.total(tensors)
+    B = 128
+    P1 = 8
+    n1 = M // P1
+    nb1 = n1 // B
+    two = levels == 2
+    P2 = 4 if two else 1
+    n2 = n1 // P2
+    nb2 = n2 // B
+    alpha1, alpha2 = (1.0, 1.0 / 32) if two else (1.0 / 8, None)
+
+    rng = np.random.default_rng(seed)
+    S = np.unique(np.concatenate([[0, nb2 - 1], rng.integers(0, nb2, size=n_sample)]))
+    L1 = (np.arange(P2)[:, None] * nb2 + S[None, :]).reshape(-1) if two else S  # level-1 blocks
+    L0 = (np.arange(P1)[:, None] * nb1 + L1[None, :]).reshape(-1)  # EF-quantize blocks
+
+    g = torch.empty(M, dtype=torch.float32, device="cuda")
+    ef = torch.zeros(M, dtype=torch.float32, device="cuda")
+    codes = torch.empty(M // 2, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(M // B, dtype=torch.float32, device="cuda")
+    chunks_c = [codes[j * n1 // 2:(j + 1) * n1 // 2] for j in range(P1)]
+    chunks_s = [scales[j * nb1:(j + 1) * nb1] for j in range(P1)]
+    if two:
+        rqc = torch.empty(n1 // 2, dtype=torch.uint8, device="cuda")
+        rqs = torch.empty(nb1, dtype=torch.float32, device="cuda")
+        out = torch.empty(n2, dtype=torch.float32, device="cuda")
+        sub_c = [rqc[i * n2 // 2:(i + 1) * n2 // 2] for i in range(P2)]
+        sub_s = [rqs[i * nb2:(i + 1) * nb2] for i in range(P2)]
+    else:
+        out = torch.empty(n1, dtype=torch.float32, device="cuda")
+
+    ef_o = np.zeros(L0.size * B, np.float32)  # oracle EF of the tracked blocks
+    for step in range(steps):
+        synth.fill_model(g, tensors, std=1e-3, seed=synth.seed_for(tag, "grad", step=step),
+                         heavy_tails=True)
+        Z().zq_quantize_ef_int4(g, ef, B, 0.9, 1.0, codes, scales)
+        if two:
+            Z().zq_dequant_reduce(chunks_c, chunks_s, n1, B, alpha1, rq_codes=rqc, rq_scales=rqs)
+            Z().zq_dequant_reduce(sub_c, sub_s, n2, B, alpha2, out=out)
+        else:
+            Z().zq_dequant_reduce(chunks_c, chunks_s, n1, B, alpha1, out=out)
+        torch.cuda.synchronize()
+
+        # oracle: EF quantize of the tracked blocks
+        g_h = gather_blocks(g, L0, B)
+        c0, s0 = O.quantize_ef_int4(g_h, ef_o, B, 0.9, 1.0)
+        what = f"{tag} step {step}"
+        assert_bits_equal(int4_block_bytes(codes, L0, B), c0, what + " codes")
+        assert_bits_equal(to_host(scales)[L0], s0, what + " scales")
+        assert_bits_equal(gather_blocks(ef, L0, B), ef_o, what + " ef")
+        # level 1: chunk j of the gathered layout = blocks j*nb1 + L1
+        m1 = L1.size * B
+        cj = [c0[j * m1 // 2:(j + 1) * m1 // 2] for j in range(P1)]
+        sj = [s0[j * L1.size:(j + 1) * L1.size] for j in range(P1)]
+        if two:
+            _, rc_o, rs_o = O.dequant_reduce(cj, sj, m1, B, alpha1, want_out=False, requant=True)
+            assert_bits_equal(int4_block_bytes(rqc, L1, B), rc_o, what + " requant codes")
+            assert_bits_equal(to_host(rqs)[L1], rs_o, what + " requant scales")
+            m2 = S.size * B
+            ci = [rc_o[i * m2 // 2:(i + 1) * m2 // 2] for i in range(P2)]
+            si = [rs_o[i * S.size:(i + 1) * S.size] for i in range(P2)]
+            out_o, _, _ = O.dequant_reduce(ci, si, m2, B, alpha2)
+        else:
+            out_o, _, _ = O.dequant_reduce(cj, sj, m1, B, alpha1)
+        got = gather_blocks(out, S, B)
+        assert np.allclose(got, out_o, rtol=1e-6, atol=0), what + " reduced sum (1e-6)"
+        assert_bits_equal(got, out_o, what + " reduced sum")
+
+
+def test_qgz_loco_0p85b_ten_steps_sampled():
+    run_two_level(synth.llama_0p85b(), "llama0p85b", steps=10, levels=1, n_sample=64, seed=4)
+
+
+def test_qgz_loco_7p5b_two_level_sampled():
+    run_two_level(synth.llama_7p5b(), "llama7p5b", steps=2, levels=2, n_sample=24, seed=5)
