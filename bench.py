@@ -201,7 +201,16 @@ def main():
                 "kernel": "efq_kernel<fp32, ef, B=128>", "bytes_per_launch": bytes_efq,
                 "avg_launch_ms": round(k_ms["efq"], 4)}
 
+    # LoCo variant: an EF buffer at the intra-node requant as well
+    rq_ef = torch.zeros(n1, dtype=torch.float32, device=dev)
+    ms_rqef = timed(torch, lambda: zq.zq_dequant_reduce(chunks_c, chunks_s, n1, B, 1.0,
+                                                        rq_codes=rq_codes, rq_scales=rq_scales,
+                                                        rq_ef=rq_ef, rq_beta_e=beta,
+                                                        rq_beta_r=1.0), 10)
+    del rq_ef
     rows = {
+        "dequant_reduce_requant_ef_p8_b128_7.5B": row(
+            dr_bytes(n1, B, P1, out=False, rq=True, rq_ef=True), ms_rqef, n1),
         "efq_fp32_b128_7.5B": row(bytes_efq, k_ms["efq"], M),
         "dequant_reduce_requant_p8_b128_7.5B": row(bytes_dr_rq, k_ms["dr_rq"], n1),
         "dequant_reduce_p4_b128_7.5B": row(bytes_dr, k_ms["dr"], n2),
@@ -221,6 +230,10 @@ def main():
 
     if not args.no_rows:
         rows.update(extra_rows(torch, zq, synth, dev, log))
+    ceil = ceilings(torch, dev) if not args.no_rows else None
+    if ceil:
+        roofline["ceilings_measured"] = ceil
+        roofline["frac_of_mixed_ceiling"] = round(efq_gbs / ceil["torch_add_2r1w"], 4)
 
     line = {
         "metric": METRIC,
@@ -248,6 +261,26 @@ def main():
         "rows": rows,
     }
     print(json.dumps(line), flush=True)
+
+
+def ceilings(torch, dev):
+    """Practical HBM ceilings of this GPU for each traffic mix, from torch's
+    own streaming kernels on 2^30-element fp32 buffers: read-only (sum),
+    write-only (fill), copy (1 read : 1 write) and add (2 reads : 1 write,
+    the mix closest to EF quantize's 8 B read : 4.5 B written)."""
+    n = 1 << 30
+    a = torch.randn(n, device=dev)
+    b = torch.randn(n, device=dev)
+    c = torch.empty(n, device=dev)
+    out = {
+        "torch_sum_read": 4 * n / timed(torch, lambda: a.sum(), 10) / 1e6,
+        "torch_fill_write": 4 * n / timed(torch, lambda: c.fill_(1.0), 10) / 1e6,
+        "torch_copy_1r1w": 8 * n / timed(torch, lambda: c.copy_(a), 10) / 1e6,
+        "torch_add_2r1w": 12 * n / timed(torch, lambda: torch.add(a, b, out=c), 10) / 1e6,
+    }
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {k: round(v, 1) for k, v in out.items()}
 
 
 def row(nbytes, ms, elems):

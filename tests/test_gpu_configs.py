@@ -150,10 +150,14 @@ def test_int8_weights_0p85b_sampled_blocks():
 
 # ------------------------------------------- qgZ + LoCo: 0.85B and 7.5B --
 
-def run_two_level(tensors, tag, steps, levels, n_sample, seed):
+def run_two_level(tensors, tag, steps, levels, n_sample, seed, beta=(0.9, 1.0), rq_beta=None,
+                  reset_every=None):
     """EF quantize of the whole gradient, then level-1 reduce over P1 chunks
     (with requant when there is a second level), then level-2 reduce over P2
-    sub-chunks; sampled blocks checked at every step."""
+    sub-chunks; sampled blocks checked at every step.  LoCo variants: `beta`
+    = (beta_e, beta_r) of the EF update, `rq_beta` turns on an EF buffer at
+    the requant (the per-parameter inter-level EF buffer), `reset_every`
+    zeroes the EF buffers every that many steps."""
     M = synth.total(tensors)
     B = 128
     P1 = 8
@@ -184,14 +188,24 @@ def run_two_level(tensors, tag, steps, levels, n_sample, seed):
         sub_s = [rqs[i * nb2:(i + 1) * nb2] for i in range(P2)]
     else:
         out = torch.empty(n1, dtype=torch.float32, device="cuda")
+    rq_ef = torch.zeros(n1, dtype=torch.float32, device="cuda") if rq_beta else None
+    rq_be, rq_br = rq_beta or (0.0, 1.0)
 
     ef_o = np.zeros(L0.size * B, np.float32)  # oracle EF of the tracked blocks
+    rq_ef_o = np.zeros(L1.size * B, np.float32) if rq_beta else None
     for step in range(steps):
+        if reset_every and step and step % reset_every == 0:
+            ef.zero_()
+            ef_o[:] = 0.0
+            if rq_beta:
+                rq_ef.zero_()
+                rq_ef_o[:] = 0.0
         synth.fill_model(g, tensors, std=1e-3, seed=synth.seed_for(tag, "grad", step=step),
                          heavy_tails=True)
-        Z().zq_quantize_ef_int4(g, ef, B, 0.9, 1.0, codes, scales)
+        Z().zq_quantize_ef_int4(g, ef, B, beta[0], beta[1], codes, scales)
         if two:
-            Z().zq_dequant_reduce(chunks_c, chunks_s, n1, B, alpha1, rq_codes=rqc, rq_scales=rqs)
+            Z().zq_dequant_reduce(chunks_c, chunks_s, n1, B, alpha1, rq_codes=rqc, rq_scales=rqs,
+                                  rq_ef=rq_ef, rq_beta_e=rq_be, rq_beta_r=rq_br)
             Z().zq_dequant_reduce(sub_c, sub_s, n2, B, alpha2, out=out)
         else:
             Z().zq_dequant_reduce(chunks_c, chunks_s, n1, B, alpha1, out=out)
@@ -199,7 +213,7 @@ def run_two_level(tensors, tag, steps, levels, n_sample, seed):
 
         # oracle: EF quantize of the tracked blocks
         g_h = gather_blocks(g, L0, B)
-        c0, s0 = O.quantize_ef_int4(g_h, ef_o, B, 0.9, 1.0)
+        c0, s0 = O.quantize_ef_int4(g_h, ef_o, B, beta[0], beta[1])
         what = f"{tag} step {step}"
         assert_bits_equal(int4_block_bytes(codes, L0, B), c0, what + " codes")
         assert_bits_equal(to_host(scales)[L0], s0, what + " scales")
@@ -209,9 +223,12 @@ def run_two_level(tensors, tag, steps, levels, n_sample, seed):
         cj = [c0[j * m1 // 2:(j + 1) * m1 // 2] for j in range(P1)]
         sj = [s0[j * L1.size:(j + 1) * L1.size] for j in range(P1)]
         if two:
-            _, rc_o, rs_o = O.dequant_reduce(cj, sj, m1, B, alpha1, want_out=False, requant=True)
+            _, rc_o, rs_o = O.dequant_reduce(cj, sj, m1, B, alpha1, want_out=False, requant=True,
+                                             rq_ef=rq_ef_o, rq_beta_e=rq_be, rq_beta_r=rq_br)
             assert_bits_equal(int4_block_bytes(rqc, L1, B), rc_o, what + " requant codes")
             assert_bits_equal(to_host(rqs)[L1], rs_o, what + " requant scales")
+            if rq_beta:
+                assert_bits_equal(gather_blocks(rq_ef, L1, B), rq_ef_o, what + " requant ef")
             m2 = S.size * B
             ci = [rc_o[i * m2 // 2:(i + 1) * m2 // 2] for i in range(P2)]
             si = [rs_o[i * S.size:(i + 1) * S.size] for i in range(P2)]
@@ -229,3 +246,16 @@ def test_qgz_loco_0p85b_ten_steps_sampled():
 
 def test_qgz_loco_7p5b_two_level_sampled():
     run_two_level(synth.llama_7p5b(), "llama7p5b", steps=2, levels=2, n_sample=24, seed=5)
+
+
+def test_loco_requant_ef_7p5b_two_level_sampled():
+    """LoCo variant: an EF buffer at the intra-node requant as well (beta 0.9)."""
+    run_two_level(synth.llama_7p5b(), "llama7p5b", steps=3, levels=2, n_sample=16, seed=6,
+                  rq_beta=(0.9, 1.0))
+
+
+def test_loco_moving_average_with_reset_0p85b_sampled():
+    """LoCo variant: moving-average EF (beta, 1 - beta) with the EF buffer
+    reset every 4 steps (a caller-side zeroing between calls)."""
+    run_two_level(synth.llama_0p85b(), "llama0p85b", steps=10, levels=1, n_sample=48, seed=7,
+                  beta=(0.9, 0.1), reset_every=4)

@@ -18,6 +18,10 @@
 #include "zq_device.h"
 #include "zq_launch.h"
 
+#ifndef ZQ_DR_U
+#define ZQ_DR_U 2  // sub-vectors of 512 outputs per wave tile
+#endif
+
 namespace zq {
 namespace {
 
@@ -27,7 +31,7 @@ struct DrGeom {
     static constexpr int SUB = kWave * VEC;
     static constexpr int LPB = B <= SUB ? B / VEC : kWave;
     static constexpr int SPB = B <= SUB ? 1 : B / SUB;
-    static constexpr int U = SPB > 2 ? SPB : 2;
+    static constexpr int U = SPB > ZQ_DR_U ? SPB : ZQ_DR_U;
     static constexpr int TILE = SUB * U;
     static constexpr int BPT = TILE / B;
 };

@@ -22,9 +22,22 @@ struct Geometry {
     uint32_t max_wgs;
 };
 
-constexpr Geometry kGeomStream{64, 1u << 24};       // EF quantize, int8, SR
-constexpr Geometry kGeomReduce{256, 1u << 22};      // dequant-reduce into fp32
-constexpr Geometry kGeomReduceRequant{256, 4096};   // dequant-reduce-requant
+#ifndef ZQ_STREAM_THREADS
+#define ZQ_STREAM_THREADS 64
+#endif
+#ifndef ZQ_REDUCE_THREADS
+#define ZQ_REDUCE_THREADS 256
+#endif
+#ifndef ZQ_RQ_THREADS
+#define ZQ_RQ_THREADS 256
+#endif
+#ifndef ZQ_RQ_MAX_WGS
+#define ZQ_RQ_MAX_WGS 4096
+#endif
+
+constexpr Geometry kGeomStream{ZQ_STREAM_THREADS, 1u << 24};          // EF quantize, int8, SR
+constexpr Geometry kGeomReduce{ZQ_REDUCE_THREADS, 1u << 22};          // dequant-reduce into fp32
+constexpr Geometry kGeomReduceRequant{ZQ_RQ_THREADS, ZQ_RQ_MAX_WGS};  // dequant-reduce-requant
 
 inline dim3 grid_for_tiles(size_t tiles, Geometry g) {
     const size_t per_wg = g.threads / 64;
