@@ -420,6 +420,22 @@ def kernel_table():
     print(f"{lib}  GB/s: " + "  ".join(f"{k} {v:.0f}" for k, v in res.items()), flush=True)
 
 
+def timed_burst(torch, fn, reps, warm=2):
+    """Average ms per call over `reps` back-to-back calls between two events
+    (host enqueue time hides behind the GPU when the GPU is the slower)."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def timed(torch, fn, reps, warm=2):
     for _ in range(warm):
         fn()
@@ -448,9 +464,9 @@ def extra_rows(torch, zq, synth, dev, log):
     c8 = torch.empty(n, dtype=torch.int8, device=dev)
     s8 = torch.empty(zq.num_blocks(n, 2048), dtype=torch.float32, device=dev)
     wd = torch.empty(n, dtype=torch.bfloat16, device=dev)
-    ms = timed(torch, lambda: zq.zq_quant_int8(w, 2048, c8, s8), 20)
+    ms = timed_burst(torch, lambda: zq.zq_quant_int8(w, 2048, c8, s8), 20)
     rows["quant_int8_bf16_b2048_0.85B"] = row(n * 3 + 4 * s8.numel(), ms, n)
-    ms = timed(torch, lambda: zq.zq_dequant_int8(c8, s8, 2048, wd), 20)
+    ms = timed_burst(torch, lambda: zq.zq_dequant_int8(c8, s8, 2048, wd), 20)
     rows["dequant_int8_bf16_b2048_0.85B"] = row(n * 3 + 4 * s8.numel(), ms, n)
     log("int8 rows", rows["quant_int8_bf16_b2048_0.85B"], rows["dequant_int8_bf16_b2048_0.85B"])
     del w, c8, s8, wd
@@ -462,12 +478,12 @@ def extra_rows(torch, zq, synth, dev, log):
     cq = torch.empty(n // 2, dtype=torch.uint8, device=dev)
     sq = torch.empty(n // 128, dtype=torch.float32, device=dev)
     outq = torch.empty(n // 8, dtype=torch.float32, device=dev)
-    ms = timed(torch, lambda: zq.zq_quantize_ef_int4(gq, efq_, 128, 0.9, 1.0, cq, sq), 10)
+    ms = timed_burst(torch, lambda: zq.zq_quantize_ef_int4(gq, efq_, 128, 0.9, 1.0, cq, sq), 10)
     rows["efq_fp32_b128_0.85B"] = row(efq_bytes(n, 128, 4), ms, n)
     nc = n // 8
     cc = [cq[j * nc // 2:(j + 1) * nc // 2] for j in range(8)]
     ss = [sq[j * nc // 128:(j + 1) * nc // 128] for j in range(8)]
-    ms = timed(torch, lambda: zq.zq_dequant_reduce(cc, ss, nc, 128, 0.125, out=outq), 20)
+    ms = timed_burst(torch, lambda: zq.zq_dequant_reduce(cc, ss, nc, 128, 0.125, out=outq), 20)
     rows["dequant_reduce_p8_b128_0.85B"] = row(dr_bytes(nc, 128, 8), ms, nc)
     log("0.85B qgZ rows", rows["efq_fp32_b128_0.85B"], rows["dequant_reduce_p8_b128_0.85B"])
     del gq, efq_, cq, sq, outq, cc, ss
@@ -478,17 +494,49 @@ def extra_rows(torch, zq, synth, dev, log):
     dst = torch.zeros(n, dtype=torch.bfloat16, device=dev)
     src = torch.empty(n, dtype=torch.bfloat16, device=dev)
     synth.fill_model(src, t2, std=1e-4, seed=synth.seed_for("gpt2", "grad", mb=0))
-    ms = timed(torch, lambda: zq.zq_sr_accumulate(dst, src, 0, 0), 20)
+    ms = timed_burst(torch, lambda: zq.zq_sr_accumulate(dst, src, 0, 0), 20)
     rows["sr_accumulate_bf16_gpt2_124M_full"] = row(6 * n, ms, n)
     shard = n // 8
     off = 3 * shard
     dsh = torch.zeros(shard, dtype=torch.bfloat16, device=dev)
     ssh = src[off:off + shard]
-    ms = timed(torch, lambda: zq.zq_sr_accumulate(dsh, ssh, 0, off), 50)
+    st = torch.cuda.current_stream().cuda_stream
+    dp, sp = dsh.data_ptr(), ssh.data_ptr()
+    ms = timed_burst(torch, lambda: zq.lib.zq_sr_accumulate(dp, sp, shard, 0, off, 0, st), 200)
     rows["sr_accumulate_bf16_gpt2_rank3_shard"] = dict(row(6 * shard, ms, shard),
                                                        note="cache-resident (93 MB)")
     log("SR rows", rows["sr_accumulate_bf16_gpt2_124M_full"])
     del dst, src, dsh, ssh
+
+    # llm.c's per-tensor ZeRO-2 loop for rank 3 of 8 over GPT-2's 148 tensors:
+    # SR-add each tensor's shard slice and clear each whole reduced buffer --
+    # one batched call against 148 single calls + 148 zero fills.
+    grads = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    synth.fill_model(grads, t2, std=1e-4, seed=synth.seed_for("gpt2", "grad", mb=0))
+    shards = torch.zeros(n // 8, dtype=torch.bfloat16, device=dev)
+    segs, off, soff = [], 0, 0
+    for i, t in enumerate(t2):
+        m = t.numel // 8
+        segs.append((shards[soff:soff + m], grads[off:off + t.numel], m, 3 * m, i, off + 3 * m))
+        off += t.numel
+        soff += m
+    nbytes = sum(6 * m + 2 * src.numel() for _, src, m, _, _, _ in segs)
+    table = zq.SrSegmentTable(segs)
+    ms_b = timed_burst(torch, lambda: zq.zq_sr_accumulate_batched(table, zero_src=True), 50)
+
+    def loop():
+        for d_, s_, m_, o_, sd_, cb_ in segs:
+            zq.zq_sr_accumulate(d_, s_[o_:o_ + m_], sd_, cb_)
+            s_.zero_()
+    ms_l = timed_burst(torch, loop, 5)
+    rows["sr_accumulate_batched_gpt2_148_tensors_rank3"] = dict(
+        row(nbytes, ms_b, n // 8),
+        note=f"one call for 148 tensors incl. clearing the reduced buffers (marshalled table, "
+             f"back-to-back calls); the same work as a Python loop of 148 single calls + 148 "
+             f"torch zero_() takes {ms_l:.3f} ms, host overhead included",
+        python_loop_ms=round(ms_l, 4))
+    log("batched SR", rows["sr_accumulate_batched_gpt2_148_tensors_rank3"])
+    del grads, shards, segs
 
     # 4 simulated ranks, bf16 2^20 each, block 256 (cache-resident, launch-bound)
     n = 4 << 20
@@ -497,7 +545,10 @@ def extra_rows(torch, zq, synth, dev, log):
     e4 = torch.zeros(n, dtype=torch.float32, device=dev)
     c4 = torch.empty(n // 2, dtype=torch.uint8, device=dev)
     s4 = torch.empty(n // 256, dtype=torch.float32, device=dev)
-    ms = timed(torch, lambda: zq.zq_quantize_ef_int4(g4, e4, 256, 1.0, 1.0, c4, s4), 50)
+    st = torch.cuda.current_stream().cuda_stream
+    a4 = (g4.data_ptr(), e4.data_ptr(), c4.data_ptr(), s4.data_ptr())
+    ms = timed_burst(torch, lambda: zq.lib.zq_quantize_ef_int4(a4[0], 1, a4[1], n, 256, 1.0, 1.0,
+                                                               a4[2], a4[3], st), 200)
     rows["efq_bf16_b256_4x2^20"] = dict(row(efq_bytes(n, 256, 2), ms, n),
                                        note="cache-resident (44 MB)")
     torch.cuda.empty_cache()

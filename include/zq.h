@@ -174,6 +174,42 @@ zq_status zq_dequant_int8(const int8_t *codes, const float *scales, size_t n, ui
 zq_status zq_sr_accumulate(uint16_t *dst_bf16, uint16_t *src_bf16, size_t n, uint64_t seed,
                            uint64_t counter_base, int zero_src, void *stream);
 
+/*
+ * zq_sr_accumulate_batched -- the per-tensor loop of llm.c's ZeRO-2 gradient
+ * accumulation in one call ([llm.c] review of llmc/zero.cuh: for each tensor
+ * i, vector_add(shard_i, reduced_i + rank * n_i, n_i, seed + i) followed by a
+ * memset of the whole reduced_i -- tiny back-to-back kernels whose idle gaps
+ * the reviewers point out, and the memset that could be fused into the add).
+ *
+ * Segment i does exactly what zq_sr_accumulate(seg.dst, seg.src +
+ * seg.src_offset, seg.n, seg.seed, seg.counter_base, 0) does, and then, when
+ * zero_src != 0, sets ALL seg.src_len elements of seg.src to 0 (the read
+ * slice after it is read).  Segments run in one pass, up to 32 per kernel
+ * launch (the table travels in the kernel arguments; nothing is allocated).
+ *
+ *   segs      HOST array of n_seg segments (read during the call only).
+ *   dst       [n] bf16 accumulator, 16-byte aligned.
+ *   src       [src_len] bf16 reduced buffer, 16-byte aligned; src_offset is
+ *             a multiple of 8 and src_offset + n <= src_len.
+ *   seed, counter_base   as in zq_sr_accumulate (counter_base + n <= 2^64 - 1).
+ * Errors: ZQ_ERR_NULL (segs NULL with n_seg > 0, or a NULL buffer of a
+ * non-empty segment), ZQ_ERR_SIZE (offset / length / counter overflow, a
+ * segment longer than 2^40 elements, or n_seg > 65536), ZQ_ERR_ALIGN, ZQ_ERR_ALIAS (any written range -- a dst, or
+ * a src buffer when zero_src -- overlapping any other segment's range).
+ */
+typedef struct {
+    uint16_t *dst;
+    uint16_t *src;
+    uint64_t n;
+    uint64_t src_offset;
+    uint64_t src_len;
+    uint64_t seed;
+    uint64_t counter_base;
+} zq_sr_segment;
+
+zq_status zq_sr_accumulate_batched(const zq_sr_segment *segs, uint32_t n_seg, int zero_src,
+                                   void *stream);
+
 /* Host-only helpers (no device work, usable without a GPU). */
 size_t zq_int4_code_bytes(size_t n);               /* ceil(n/2)                        */
 size_t zq_num_blocks(size_t n, uint32_t block);    /* ceil(n/block); 0 if block == 0   */

@@ -219,3 +219,19 @@ def volume_bytes(M: int, block_w: int, block_g: int):
     o = np.zeros(2, dtype=np.uint64)
     lib().orc_volume_bytes(M, block_w, block_g, _ptr(o))
     return int(o[0]), int(o[1])
+
+
+def sr_accumulate_segments(segments, zero_src: bool):
+    """llm.c's per-tensor ZeRO-2 loop ("Zero 2 #593", review of
+    llmc/zero.cuh): for each segment (dst, src, n, src_offset, seed,
+    counter_base), dst[0:n] += src[src_offset:src_offset+n] with stochastic
+    rounding, then -- with zero_src -- the whole src buffer is cleared (the
+    memset the review suggests folding into the add).  In place on the given
+    uint16 (bf16 bit) arrays."""
+    for dst, src, n, off, seed, cb in segments:
+        if n:
+            sl = src[off:off + n]
+            assert sl.flags["C_CONTIGUOUS"]
+            sr_accumulate(dst[:n], sl, seed, cb, zero_src=False)
+        if zero_src:
+            src[:] = 0

@@ -17,7 +17,8 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails va
 def test_exports_every_declared_symbol():
     names = zq.declared_symbols()
     assert set(names) == {"zq_quantize_ef_int4", "zq_dequant_reduce", "zq_quant_int8",
-                          "zq_dequant_int8", "zq_sr_accumulate", "zq_int4_code_bytes",
+                          "zq_dequant_int8", "zq_sr_accumulate", "zq_sr_accumulate_batched",
+                          "zq_int4_code_bytes",
                           "zq_num_blocks", "zq_status_str", "zq_abi_version"}
     for name in names:
         assert hasattr(L, name), name
@@ -125,3 +126,31 @@ def test_binding_guards_reject_short_or_host_buffers():
     with pytest.raises(ValueError):
         zq.zq_quantize_ef_int4(torch.zeros(16), None, 32, 1.0, 1.0, torch.zeros(8, dtype=torch.uint8),
                                torch.zeros(1))
+
+
+def test_sr_batched_validation():
+    Seg = zq.SrSegment
+
+    def call(segs, zero=0, n_seg=None):
+        arr = (Seg * max(len(segs), 1))(*segs)
+        return L.zq_sr_accumulate_batched(C.cast(arr, C.c_void_p), len(segs) if n_seg is None else n_seg,
+                                          zero, None)
+
+    ok = Seg(FAKE, FAKE + 0x100000, 100, 8, 200, 1, 0)
+    assert L.zq_sr_accumulate_batched(None, 0, 0, None) == zq.ZQ_OK
+    assert L.zq_sr_accumulate_batched(None, 3, 0, None) == zq.ZQ_ERR_NULL
+    assert call([ok], n_seg=70000) == zq.ZQ_ERR_SIZE
+    assert call([Seg(FAKE, FAKE + 0x100000, 100, 8, 50, 1, 0)]) == zq.ZQ_ERR_SIZE  # slice past src_len
+    assert call([Seg(FAKE, FAKE + 0x100000, 100, 8, 200, 1, (1 << 64) - 50)]) == zq.ZQ_ERR_SIZE
+    assert call([Seg(None, FAKE + 0x100000, 100, 8, 200, 1, 0)]) == zq.ZQ_ERR_NULL
+    assert call([Seg(FAKE, None, 100, 8, 200, 1, 0)]) == zq.ZQ_ERR_NULL
+    assert call([Seg(FAKE + 2, FAKE + 0x100000, 100, 8, 200, 1, 0)]) == zq.ZQ_ERR_ALIGN
+    assert call([Seg(FAKE, FAKE + 0x100000, 100, 4, 200, 1, 0)]) == zq.ZQ_ERR_ALIGN  # offset % 8
+    # two segments whose dst overlap
+    assert call([ok, Seg(FAKE + 0x40, FAKE + 0x200000, 100, 0, 100, 1, 0)]) == zq.ZQ_ERR_ALIAS
+    # reading the same slice twice is allowed, clearing it while another reads it is not
+    a = Seg(FAKE, FAKE + 0x100000, 100, 8, 200, 1, 0)
+    b = Seg(FAKE + 0x10000, FAKE + 0x100000, 100, 8, 200, 2, 0)
+    assert call([a, b], zero=1) == zq.ZQ_ERR_ALIAS
+    # a dst inside another segment's read slice
+    assert call([a, Seg(FAKE + 0x100000 + 0x20, FAKE + 0x300000, 8, 0, 8, 1, 0)]) == zq.ZQ_ERR_ALIAS

@@ -259,3 +259,54 @@ def test_loco_moving_average_with_reset_0p85b_sampled():
     reset every 4 steps (a caller-side zeroing between calls)."""
     run_two_level(synth.llama_0p85b(), "llama0p85b", steps=10, levels=1, n_sample=48, seed=7,
                   beta=(0.9, 0.1), reset_every=4)
+
+
+# ------------------------------- llm.c per-tensor ZeRO-2 accumulate, batched --
+
+def gpt2_segments(grads, shards, tensors, rank, P, mb):
+    """llm.c's per-tensor loop on the flat GPT-2 buffers: tensor i's reduced
+    buffer is grads[off_i : off_i + nelem_i]; its shard (nelem_i / P
+    elements at rank * n_i) accumulates into shards[soff_i : soff_i + n_i];
+    the random numbers are those of the shard's global indices."""
+    segs, off, soff = [], 0, 0
+    for i, t in enumerate(tensors):
+        n = t.numel // P
+        segs.append((shards[soff:soff + n], grads[off:off + t.numel], n, rank * n,
+                     (mb << 16) + i, off + rank * n))
+        off += t.numel
+        soff += n
+    return segs
+
+
+def test_gpt2_per_tensor_zero2_batched():
+    tensors = synth.gpt2_124m()
+    n = synth.total(tensors)
+    P, rank = 8, 3
+    grads = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    grads_b = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    shards = torch.zeros(n // P, dtype=torch.bfloat16, device="cuda")
+    shards_b = torch.zeros(n // P, dtype=torch.bfloat16, device="cuda")
+    rng = np.random.default_rng(8)
+    pick = sorted(set([0, len(tensors) - 1] + list(rng.integers(0, len(tensors), size=10))))
+    exp = {}
+    for mb in range(8):
+        synth.fill_model(grads, tensors, std=1e-4, seed=synth.seed_for("gpt2", "grad", mb=mb))
+        grads_b.copy_(grads)
+        segs = gpt2_segments(grads, shards, tensors, rank, P, mb)
+        host = {i: (to_host(segs[i][1]).copy()) for i in pick}
+        Z().zq_sr_accumulate_batched(segs, zero_src=True)
+        for dst, src, m, off, seed, cb in gpt2_segments(grads_b, shards_b, tensors, rank, P, mb):
+            Z().zq_sr_accumulate(dst, src[off:off + m], seed, cb)
+            src.zero_()
+        torch.cuda.synchronize()
+        assert int(grads.view(torch.int16).abs().max()) == 0, "reduced buffers not cleared"
+        for i in pick:
+            _, _, m, off, seed, cb = segs[i]
+            if i not in exp:
+                exp[i] = np.zeros(m, np.uint16)
+            O.sr_accumulate(exp[i], host[i][off:off + m].copy(), seed, cb)
+    assert torch.equal(shards.view(torch.int16), shards_b.view(torch.int16)), \
+        "batched call differs from the per-tensor loop"
+    segs = gpt2_segments(grads, shards, tensors, rank, P, 0)
+    for i in pick:
+        assert_bits_equal(to_host(segs[i][0]), exp[i], f"tensor {i} ({tensors[i].name}) shard")

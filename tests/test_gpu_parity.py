@@ -312,3 +312,57 @@ def test_sr_shard_equals_slice_of_full_run_on_gpu():
         Z().zq_sr_accumulate(part, src[off:off + shard].contiguous(), m, off)
     torch.cuda.synchronize()
     assert torch.equal(full[off:off + shard].view(torch.int16), part.view(torch.int16))
+
+
+# ------------------------------------------------ batched SR accumulation --
+
+@pytest.mark.parametrize("zero_src", [False, True])
+def test_sr_batched_matches_oracle(zero_src):
+    """70 segments (three launches of at most 32), ragged lengths, zero-length
+    segments, every counter phase, slices anywhere in their buffers."""
+    rng = np.random.default_rng(21 + zero_src)
+    segs_g, segs_o = [], []
+    for i in range(70):
+        n = int(rng.choice([0, 1, 7, 8, 1000, 1024, 3000, 20000]))
+        off = 8 * int(rng.integers(0, 300))
+        tail = int(rng.integers(0, 2000))
+        L = off + n + tail
+        d = sr_inputs(max(n, 1), seed=100 + i)[0][:n].copy()
+        s = sr_inputs(max(L, 1), seed=200 + i)[1][:L].copy()
+        seed = int(rng.integers(0, 2 ** 63))
+        cb = int(rng.integers(0, 2 ** 40))
+        segs_o.append((d, s, n, off, seed, cb))
+        segs_g.append((to_gpu(d) if n else torch.zeros(8, dtype=torch.bfloat16, device="cuda"),
+                       to_gpu(s) if L else torch.zeros(8, dtype=torch.bfloat16, device="cuda"),
+                       n, off, seed, cb))
+    expect = [(d.copy(), s.copy(), n, off, seed, cb) for d, s, n, off, seed, cb in segs_o]
+    O.sr_accumulate_segments(expect, zero_src)
+    Z().zq_sr_accumulate_batched(segs_g, zero_src=zero_src)
+    torch.cuda.synchronize()
+    for i, ((dg, sg, n, off, _, _), (de, se, _, _, _, _)) in enumerate(zip(segs_g, expect)):
+        if n:
+            assert_bits_equal(to_host(dg)[:n], de, f"segment {i} dst")
+        if se.size:
+            assert_bits_equal(to_host(sg)[:se.size], se, f"segment {i} src")
+
+
+def test_sr_batched_equals_per_tensor_calls():
+    """The batched call gives exactly what the per-tensor loop of single
+    calls plus a zeroing of each buffer gives."""
+    rng = np.random.default_rng(5)
+    segs_a, segs_b = [], []
+    for i in range(40):
+        n = 8 * int(rng.integers(1, 3000))
+        P = 8
+        full = torch.randn(P * n, generator=torch.Generator().manual_seed(i)).mul_(1e-4).to(torch.bfloat16).cuda()
+        dst = torch.randn(n, generator=torch.Generator().manual_seed(1000 + i)).mul_(1e-2).to(torch.bfloat16).cuda()
+        segs_a.append((dst.clone(), full.clone(), n, 3 * n, 77 + i, 12345 + 3 * n))
+        segs_b.append((dst.clone(), full.clone(), n, 3 * n, 77 + i, 12345 + 3 * n))
+    Z().zq_sr_accumulate_batched(segs_a, zero_src=True)
+    for dst, full, n, off, seed, cb in segs_b:
+        Z().zq_sr_accumulate(dst, full[off:off + n], seed, cb)
+        full.zero_()
+    torch.cuda.synchronize()
+    for (da, fa, *_), (db, fb, *_) in zip(segs_a, segs_b):
+        assert torch.equal(da.view(torch.int16), db.view(torch.int16))
+        assert torch.equal(fa.view(torch.int16), fb.view(torch.int16))

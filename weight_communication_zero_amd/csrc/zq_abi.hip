@@ -4,12 +4,16 @@
 // was issued.  No state, no allocation.
 #include <stdint.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "../../include/zq.h"
 #include "zq_launch.h"
 
 namespace {
 
 constexpr size_t kMaxElems = (size_t)1 << 60;
+constexpr size_t kMaxSegElems = (size_t)1 << 40;  // per segment of a batched call
 
 bool valid_block(uint32_t b) { return b >= 32 && b <= 4096 && (b & (b - 1)) == 0; }
 
@@ -168,6 +172,57 @@ zq_status zq_sr_accumulate(uint16_t* dst_bf16, uint16_t* src_bf16, size_t n, uin
         return ZQ_ERR_ALIAS;
     return launched(zq::launch_sr_accumulate(dst_bf16, src_bf16, n, seed, counter_base,
                                              zero_src != 0, (hipStream_t)stream));
+}
+
+zq_status zq_sr_accumulate_batched(const zq_sr_segment* segs, uint32_t n_seg, int zero_src,
+                                   void* stream) {
+    if (n_seg == 0)
+        return ZQ_OK;
+    if (!segs)
+        return ZQ_ERR_NULL;
+    if (n_seg > 65536)
+        return ZQ_ERR_SIZE;
+    // Written ranges (every dst; every src buffer when zero_src) may overlap
+    // nothing else; read ranges (src slices) may overlap each other only.
+    struct Range {
+        uintptr_t lo, hi;
+        bool written;
+    };
+    std::vector<Range> ranges;
+    std::vector<zq::SrSegment> dev;
+    ranges.reserve(2 * (size_t)n_seg);
+    dev.reserve(n_seg);
+    for (uint32_t i = 0; i < n_seg; ++i) {
+        const zq_sr_segment& g = segs[i];
+        if (g.n > kMaxSegElems || g.src_len > kMaxSegElems || g.src_offset > g.src_len ||
+            g.n > g.src_len - g.src_offset || g.counter_base > UINT64_MAX - g.n)
+            return ZQ_ERR_SIZE;
+        const bool touches_src = g.n > 0 || (zero_src && g.src_len > 0);
+        if ((g.n > 0 && !g.dst) || (touches_src && !g.src))
+            return ZQ_ERR_NULL;
+        if (!aligned(g.dst, 16) || !aligned(g.src, 16) || (g.src_offset & 7u))
+            return ZQ_ERR_ALIGN;
+        if (g.n > 0)
+            ranges.push_back({(uintptr_t)g.dst, (uintptr_t)g.dst + 2 * g.n, true});
+        if (zero_src && g.src_len > 0)
+            ranges.push_back({(uintptr_t)g.src, (uintptr_t)g.src + 2 * g.src_len, true});
+        else if (g.n > 0)
+            ranges.push_back({(uintptr_t)(g.src + g.src_offset),
+                              (uintptr_t)(g.src + g.src_offset) + 2 * g.n, false});
+        dev.push_back({g.dst, g.src, g.n, g.src_offset, g.src_len, g.seed, g.counter_base});
+    }
+    std::sort(ranges.begin(), ranges.end(),
+              [](const Range& a, const Range& b) { return a.lo < b.lo; });
+    uintptr_t max_end_any = 0, max_end_written = 0;
+    for (const Range& r : ranges) {
+        if (r.lo < (r.written ? max_end_any : max_end_written))
+            return ZQ_ERR_ALIAS;
+        max_end_any = std::max(max_end_any, r.hi);
+        if (r.written)
+            max_end_written = std::max(max_end_written, r.hi);
+    }
+    return launched(zq::launch_sr_accumulate_batched(dev.data(), (uint32_t)dev.size(),
+                                                     zero_src != 0, (hipStream_t)stream));
 }
 
 size_t zq_int4_code_bytes(size_t n) { return n / 2 + (n & 1); }

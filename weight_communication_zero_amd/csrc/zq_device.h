@@ -215,7 +215,10 @@ __device__ __forceinline__ uint32_t sr_bf16(float x, uint32_t r16) {
 // (a multiple of the quantization block), walking them with a grid stride
 // when the grid is capped.
 __device__ __forceinline__ size_t wave_id() {
-    return (size_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    // threadIdx.x >> 6 is the same on every lane of a wave; say so, so that
+    // tile bases and segment lookups stay in scalar registers.
+    const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    return (size_t)blockIdx.x * (blockDim.x >> 6) + w;
 }
 __device__ __forceinline__ size_t wave_count() { return (size_t)gridDim.x * (blockDim.x >> 6); }
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }

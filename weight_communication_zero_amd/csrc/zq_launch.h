@@ -78,4 +78,18 @@ hipError_t launch_dequant_int8(const int8_t* codes, const float* scales, size_t 
 hipError_t launch_sr_accumulate(uint16_t* dst, uint16_t* src, size_t n, uint64_t seed,
                                 uint64_t counter_base, bool zero_src, hipStream_t stream);
 
+// One segment of a batched SR accumulation (validated by the ABI layer).
+struct SrSegment {
+    uint16_t* dst;
+    uint16_t* src;
+    uint64_t n;
+    uint64_t off;
+    uint64_t len;
+    uint64_t seed;
+    uint64_t cbase;
+};
+
+hipError_t launch_sr_accumulate_batched(const SrSegment* segs, uint32_t n_seg, bool zero_src,
+                                        hipStream_t stream);
+
 }  // namespace zq

@@ -127,6 +127,124 @@ const void* sr_pick(uint64_t counter_base, bool zero) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Batched segments: one launch runs the SR tiles of up to kSegsPerLaunch
+// segments and, with zero_src, the tiles that clear the rest of each
+// segment's source buffer.  The table (with cumulative tile counts) travels
+// in the kernel arguments; a wave finds its segment by a uniform scan.
+constexpr int kSegsPerLaunch = 32;
+
+struct SrBatch {
+    SrSegment seg[kSegsPerLaunch];
+    uint32_t tile_end[kSegsPerLaunch];  // cumulative tiles (SR + zeroing) through segment s;
+                                        // unused entries hold UINT32_MAX
+    uint32_t sr_tiles[kSegsPerLaunch];  // SR tiles of segment s; the rest clear its buffer
+    uint32_t total;                     // tiles of this launch (< 2^32 by construction)
+    uint32_t zero;
+};
+
+template <int PHASE>
+__device__ __forceinline__ void sr_group(const SrSegment& g, uint64_t e0, bool zero) {
+    uint16_t* dst = g.dst;
+    uint16_t* src = g.src + g.off;
+    const uint32_t k0 = (uint32_t)g.seed, k1 = (uint32_t)(g.seed >> 32);
+    uint32_t r[8];
+    r16x8<PHASE>((g.cbase >> 3) + (e0 >> 3), k0, k1, r);
+    if (e0 + 8 <= g.n) {
+        const u4 d = ld_stream((const u4*)(dst + e0));
+        const u4 s = ld_stream((const u4*)(src + e0));
+        const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+        const uint32_t sw[4] = {s.x, s.y, s.z, s.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const float x0 = bf16lo(dw[h]) + bf16lo(sw[h]);
+            const float x1 = bf16hi(dw[h]) + bf16hi(sw[h]);
+            o[h] = sr_bf16(x0, r[2 * h]) | (sr_bf16(x1, r[2 * h + 1]) << 16);
+        }
+        st_stream(u4{o[0], o[1], o[2], o[3]}, (u4*)(dst + e0));
+        if (zero)
+            st_stream(u4{0u, 0u, 0u, 0u}, (u4*)(src + e0));
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (e0 + j < g.n) {
+                const float x = bf16lo(dst[e0 + j]) + bf16lo(src[e0 + j]);
+                dst[e0 + j] = (uint16_t)sr_bf16(x, r[j]);
+                if (zero)
+                    src[e0 + j] = 0;
+            }
+        }
+    }
+}
+
+// The counter phase (cbase & 7) is uniform per segment: one switch picks the
+// specialised random-number layout.
+__device__ __forceinline__ void sr_seg_tile(const SrSegment& g, uint64_t local, bool zero) {
+    const int lane = lane_id();
+    const uint32_t phase = __builtin_amdgcn_readfirstlane((uint32_t)(g.cbase & 7u));
+#pragma unroll
+    for (int u = 0; u < kSrU; ++u) {
+        const uint64_t e0 = local * kSrTile + (uint64_t)u * kSrSub + (uint64_t)lane * 8;
+        if (e0 >= g.n)
+            continue;
+        switch (phase) {
+            case 0: sr_group<0>(g, e0, zero); break;
+            case 1: sr_group<1>(g, e0, zero); break;
+            case 2: sr_group<2>(g, e0, zero); break;
+            case 3: sr_group<3>(g, e0, zero); break;
+            case 4: sr_group<4>(g, e0, zero); break;
+            case 5: sr_group<5>(g, e0, zero); break;
+            case 6: sr_group<6>(g, e0, zero); break;
+            default: sr_group<7>(g, e0, zero); break;
+        }
+    }
+}
+
+// Clear the part of the source buffer outside the read slice: position c of
+// the complement (length len - n) is buffer element c (before the slice) or
+// c + n (after it).
+__device__ __forceinline__ void zero_seg_tile(const SrSegment& g, uint64_t local) {
+    const int lane = lane_id();
+    const uint64_t z = g.len - g.n;
+#pragma unroll
+    for (int u = 0; u < kSrU; ++u) {
+        const uint64_t c0 = local * kSrTile + (uint64_t)u * kSrSub + (uint64_t)lane * 8;
+        if (c0 >= z)
+            continue;
+        const uint64_t p0 = c0 < g.off ? c0 : c0 + g.n;
+        const bool one_side = c0 + 8 <= g.off || c0 >= g.off;
+        if (c0 + 8 <= z && one_side && (p0 & 7u) == 0) {
+            st_stream(u4{0u, 0u, 0u, 0u}, (u4*)(g.src + p0));
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint64_t c = c0 + j;
+                if (c < z)
+                    g.src[c < g.off ? c : c + g.n] = 0;
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBlockThreads) void sr_batched_kernel(SrBatch b) {
+    for (size_t ts = wave_id(); ts < b.total; ts += wave_count()) {
+        const uint32_t t = (uint32_t)ts;
+        // Segment of tile t: the number of cumulative counts it has passed.
+        // Independent compares against table entries the compiler loads once,
+        // not a chain of dependent loads.
+        uint32_t s = 0;
+#pragma unroll
+        for (int k = 0; k < kSegsPerLaunch - 1; ++k)
+            s += t >= b.tile_end[k] ? 1u : 0u;
+        const uint32_t local = t - (s ? b.tile_end[s - 1] : 0u);
+        if (local < b.sr_tiles[s])
+            sr_seg_tile(b.seg[s], local, b.zero != 0);
+        else
+            zero_seg_tile(b.seg[s], local - b.sr_tiles[s]);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_sr_accumulate(uint16_t* dst, uint16_t* src, size_t n, uint64_t seed,
@@ -144,6 +262,43 @@ hipError_t launch_sr_accumulate(uint16_t* dst, uint16_t* src, size_t n, uint64_t
         e = hipLaunchKernel(sr_pick<true>(counter_base, zero_src), dim3(1), dim3(kWave), args, 0,
                             stream);
     return e;
+}
+
+hipError_t launch_sr_accumulate_batched(const SrSegment* segs, uint32_t n_seg, bool zero_src,
+                                        hipStream_t stream) {
+    // Segments are at most 2^40 elements (checked by the ABI layer), so a
+    // launch of up to 32 of them has fewer than 2^32 tiles.
+    uint32_t i = 0;
+    while (i < n_seg) {
+        SrBatch b = {};
+        b.zero = zero_src ? 1u : 0u;
+        uint32_t nseg = 0;
+        uint64_t tiles = 0;
+        while (i < n_seg && nseg < (uint32_t)kSegsPerLaunch) {
+            const SrSegment& g = segs[i++];
+            const uint64_t sr = (g.n + kSrTile - 1) / kSrTile;
+            const uint64_t zt = zero_src ? (g.len - g.n + kSrTile - 1) / kSrTile : 0;
+            if (sr + zt == 0)
+                continue;
+            b.seg[nseg] = g;
+            b.sr_tiles[nseg] = (uint32_t)sr;
+            tiles += sr + zt;
+            b.tile_end[nseg] = (uint32_t)tiles;
+            ++nseg;
+        }
+        if (nseg == 0)
+            continue;
+        for (uint32_t k = nseg; k < (uint32_t)kSegsPerLaunch; ++k)
+            b.tile_end[k] = UINT32_MAX;
+        b.total = (uint32_t)tiles;
+        void* args[] = {(void*)&b};
+        const hipError_t e = hipLaunchKernel((const void*)&sr_batched_kernel,
+                                             grid_for_tiles(tiles, kGeomStream),
+                                             dim3(kGeomStream.threads), args, 0, stream);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace zq

@@ -30,6 +30,13 @@ ZQ_OK, ZQ_ERR_NULL, ZQ_ERR_SIZE, ZQ_ERR_BLOCK, ZQ_ERR_ALIGN = 0, 1, 2, 3, 4
 ZQ_ERR_ALIAS, ZQ_ERR_PEERS, ZQ_ERR_DTYPE, ZQ_ERR_LAUNCH = 5, 6, 7, 8
 
 
+class SrSegment(C.Structure):
+    """zq_sr_segment of include/zq.h."""
+    _fields_ = [("dst", C.c_void_p), ("src", C.c_void_p), ("n", C.c_uint64),
+                ("src_offset", C.c_uint64), ("src_len", C.c_uint64), ("seed", C.c_uint64),
+                ("counter_base", C.c_uint64)]
+
+
 class ZQError(RuntimeError):
     def __init__(self, fn: str, status: int):
         super().__init__(f"{fn} failed: {lib.zq_status_str(status).decode()}")
@@ -51,6 +58,8 @@ def _load() -> C.CDLL:
     for f in ("zq_quantize_ef_int4", "zq_dequant_reduce", "zq_quant_int8", "zq_dequant_int8",
               "zq_sr_accumulate"):
         getattr(L, f).restype = i32
+    L.zq_sr_accumulate_batched.argtypes = [vp, u32, i32, vp]
+    L.zq_sr_accumulate_batched.restype = i32
     L.zq_int4_code_bytes.argtypes = [sz]
     L.zq_int4_code_bytes.restype = sz
     L.zq_num_blocks.argtypes = [sz, u32]
@@ -202,3 +211,31 @@ def zq_sr_accumulate(dst, src, seed: int, counter_base: int = 0, zero_src: bool 
     _check("zq_sr_accumulate",
            lib.zq_sr_accumulate(_p(dst), _p(src), n, seed, counter_base, 1 if zero_src else 0,
                                 _stream(stream)))
+
+
+class SrSegmentTable:
+    """A marshalled segment table for zq_sr_accumulate_batched: build it once
+    for a fixed set of buffers and pass it to every call (the tensors are
+    kept alive by the table)."""
+
+    def __init__(self, segments):
+        self.segments = list(segments)
+        self.arr = (SrSegment * max(len(self.segments), 1))()
+        for i, (dst, src, n, off, seed, cb) in enumerate(self.segments):
+            _need("dst", dst, n, _BF16)
+            _need("src", src, off + n, _BF16)
+            src_len = src.numel() if not isinstance(src, int) else off + n
+            self.arr[i] = SrSegment(_p(dst), _p(src), n, off, src_len, seed, cb)
+        self.ptr = C.cast(self.arr, C.c_void_p)
+
+
+def zq_sr_accumulate_batched(segments, zero_src: bool = False, stream=None) -> None:
+    """Batched SR accumulation.  `segments`: an SrSegmentTable, or an iterable
+    of (dst, src, n, src_offset, seed, counter_base) with dst / src bf16
+    tensors; src is the whole per-tensor buffer (src_len = src.numel()), of
+    which elements [src_offset, src_offset + n) are added into dst[0:n]; with
+    zero_src every element of every src buffer is cleared in the same pass."""
+    table = segments if isinstance(segments, SrSegmentTable) else SrSegmentTable(segments)
+    _check("zq_sr_accumulate_batched",
+           lib.zq_sr_accumulate_batched(table.ptr, len(table.segments), 1 if zero_src else 0,
+                                        _stream(stream)))
