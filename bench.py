@@ -208,7 +208,12 @@ def main():
                                                         rq_ef=rq_ef, rq_beta_e=beta,
                                                         rq_beta_r=1.0), 10)
     del rq_ef
+    # ZeRO++ hierarchical order (4 nodes x 8 GPUs): EF quantize into permuted partitions
+    slots = zq.zeropp_slots(P1, P2)
+    ms_perm = timed(torch, lambda: zq.zq_quantize_ef_int4_permuted(g, ef, B, beta, 1.0, codes,
+                                                                   scales, slots), 10)
     rows = {
+        "efq_permuted_zeropp_4x8_fp32_b128_7.5B": row(bytes_efq, ms_perm, M),
         "dequant_reduce_requant_ef_p8_b128_7.5B": row(
             dr_bytes(n1, B, P1, out=False, rq=True, rq_ef=True), ms_rqef, n1),
         "efq_fp32_b128_7.5B": row(bytes_efq, k_ms["efq"], M),

@@ -100,6 +100,31 @@ zq_status zq_quantize_ef_int4(const void *g, zq_dtype g_dtype, float *ef, size_t
                               float *scales, void *stream);
 
 /*
+ * zq_quantize_ef_int4_permuted -- zq_quantize_ef_int4 writing its codes and
+ * scales in a permuted partition order, so that after the two all-to-alls of
+ * hierarchical qgZ every rank holds its own contiguous partition ([ZeRO++]
+ * section 1.2: gradients are reduced inside the node first, then across
+ * nodes; the slices are reordered before quantization for that).
+ *
+ * The n elements are n_part equal partitions of part_len = n / n_part
+ * elements.  Partition p's codes and scales are written where partition
+ * slot_of_part[p] would be in zq_quantize_ef_int4's output; g and ef keep
+ * their natural order.  With intra GPUs per node and inter nodes (n_part =
+ * intra * inter, rank r = node * intra + local), ZeRO++'s order is
+ * slot_of_part[node * intra + local] = local * inter + node.
+ *
+ *   n_part        1 .. 256; part_len must be a multiple of block and at least
+ *                 max(1024, block) (ZQ_ERR_SIZE otherwise).
+ *   slot_of_part  HOST array of n_part distinct values in [0, n_part)
+ *                 (ZQ_ERR_SIZE if not a permutation).
+ * Other arguments and errors as zq_quantize_ef_int4.
+ */
+zq_status zq_quantize_ef_int4_permuted(const void *g, zq_dtype g_dtype, float *ef, size_t n,
+                                       uint32_t block, float beta_e, float beta_r, uint8_t *codes,
+                                       float *scales, uint32_t n_part,
+                                       const uint32_t *slot_of_part, void *stream);
+
+/*
  * zq_dequant_reduce -- qgZ receive side: dequantize the P int4 chunks an
  * all-to-all delivers to this GPU and reduce them in full precision, with an
  * optional requantization for the next level of the hierarchy ([ZeRO++]

@@ -235,3 +235,23 @@ def sr_accumulate_segments(segments, zero_src: bool):
             sr_accumulate(dst[:n], sl, seed, cb, zero_src=False)
         if zero_src:
             src[:] = 0
+
+
+def quantize_ef_int4_permuted(g, ef, block: int, beta_e: float, beta_r: float, slot_of_part):
+    """The EF int4 quantizer with its outputs in permuted partition order
+    ("ZeROPlusPlus.md" notes, section 1.2: hierarchical gradient reduction,
+    inside the node first, then across nodes): the plain quantizer, then the
+    codes and scales of partition p placed where partition slot_of_part[p]
+    would be.  Partitions are equal and whole blocks long."""
+    n = np.asarray(g).size
+    n_part = len(slot_of_part)
+    part = n // n_part
+    assert part * n_part == n and part % block == 0 and part % 2 == 0
+    codes, scales = quantize_ef_int4(g, ef, block, beta_e, beta_r)
+    c_out = np.empty_like(codes)
+    s_out = np.empty_like(scales)
+    cb, sb = part // 2, part // block
+    for p, slot in enumerate(slot_of_part):
+        c_out[slot * cb:(slot + 1) * cb] = codes[p * cb:(p + 1) * cb]
+        s_out[slot * sb:(slot + 1) * sb] = scales[p * sb:(p + 1) * sb]
+    return c_out, s_out

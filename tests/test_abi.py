@@ -16,7 +16,8 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails va
 
 def test_exports_every_declared_symbol():
     names = zq.declared_symbols()
-    assert set(names) == {"zq_quantize_ef_int4", "zq_dequant_reduce", "zq_quant_int8",
+    assert set(names) == {"zq_quantize_ef_int4", "zq_quantize_ef_int4_permuted",
+                          "zq_dequant_reduce", "zq_quant_int8",
                           "zq_dequant_int8", "zq_sr_accumulate", "zq_sr_accumulate_batched",
                           "zq_int4_code_bytes",
                           "zq_num_blocks", "zq_status_str", "zq_abi_version"}
@@ -154,3 +155,25 @@ def test_sr_batched_validation():
     assert call([a, b], zero=1) == zq.ZQ_ERR_ALIAS
     # a dst inside another segment's read slice
     assert call([a, Seg(FAKE + 0x100000 + 0x20, FAKE + 0x300000, 8, 0, 8, 1, 0)]) == zq.ZQ_ERR_ALIAS
+
+
+def test_permuted_quantize_validation():
+    def call(n=8 * 1024, block=128, n_part=8, slots=None, g=FAKE, codes=FAKE + 0x1000000,
+             scales=FAKE + 0x2000000):
+        slots = list(range(n_part)) if slots is None else slots
+        arr = (C.c_uint32 * max(len(slots), 1))(*slots)
+        return L.zq_quantize_ef_int4_permuted(g, 0, None, n, block, 1.0, 1.0, codes, scales,
+                                              n_part, C.cast(arr, C.c_void_p), None)
+    assert call(block=96) == zq.ZQ_ERR_BLOCK
+    assert call(n_part=0, slots=[0]) == zq.ZQ_ERR_SIZE
+    assert call(n_part=257, slots=list(range(257))) == zq.ZQ_ERR_SIZE
+    assert call(n=8 * 1024 + 8) == zq.ZQ_ERR_SIZE            # not n_part equal partitions
+    assert call(n=8 * 512) == zq.ZQ_ERR_SIZE                 # partition shorter than 1024
+    assert call(n=8 * 1088, block=128) == zq.ZQ_ERR_SIZE    # partition not whole blocks
+    assert call(slots=[0, 1, 2, 3, 4, 5, 6, 6]) == zq.ZQ_ERR_SIZE  # not a permutation
+    assert call(slots=[0, 1, 2, 3, 4, 5, 6, 8]) == zq.ZQ_ERR_SIZE
+    assert call(g=None) == zq.ZQ_ERR_NULL
+    assert call(n=0, g=None) == zq.ZQ_OK
+    assert call(codes=FAKE + 0x1000002) == zq.ZQ_ERR_ALIGN
+    assert call(codes=FAKE + 0x100) == zq.ZQ_ERR_ALIAS
+    assert zq.zeropp_slots(4, 2) == [0, 2, 4, 6, 1, 3, 5, 7]

@@ -366,3 +366,91 @@ def test_sr_batched_equals_per_tensor_calls():
     for (da, fa, *_), (db, fb, *_) in zip(segs_a, segs_b):
         assert torch.equal(da.view(torch.int16), db.view(torch.int16))
         assert torch.equal(fa.view(torch.int16), fb.view(torch.int16))
+
+
+# -------------------------------------- permuted (ZeRO++ hierarchical) order --
+
+@pytest.mark.parametrize("block", [128, 256, 2048])
+@pytest.mark.parametrize("gdt", ["fp32", "bf16"])
+def test_efq_permuted_matches_oracle(block, gdt):
+    rng = np.random.default_rng(block + (gdt == "bf16"))
+    for n_part, part in [(1, max(1024, block)), (5, max(1152, block * 3 // 2 // block * block or block)),
+                         (8, max(2048, block)), (32, max(1024, block) + block)]:
+        part = (part // block) * block
+        n = n_part * part
+        slots = [int(v) for v in rng.permutation(n_part)]
+        x = grad_values(n, seed=n + block, special=True, block=block)
+        g = as_bf16_bits(x) if gdt == "bf16" else x
+        for with_ef in (False, True):
+            ef_h = grad_values(n, seed=3, std=1e-5) if with_ef else None
+            ef_o = ef_h.copy() if with_ef else None
+            c_o, s_o = O.quantize_ef_int4_permuted(g, ef_o, block, 0.9, 1.0, slots)
+            ef_g = to_gpu(ef_h) if with_ef else None
+            codes = Guarded((n + 1) // 2, torch.uint8)
+            scales = Guarded(n // block, torch.float32)
+            Z().zq_quantize_ef_int4_permuted(to_gpu(g), ef_g, block, 0.9, 1.0, codes.t, scales.t,
+                                             slots)
+            torch.cuda.synchronize()
+            what = f"permuted n_part={n_part} part={part} B={block} {gdt} ef={with_ef}"
+            assert_bits_equal(codes.host(), c_o, what + " codes")
+            assert_bits_equal(scales.host(), s_o, what + " scales")
+            if with_ef:
+                assert_bits_equal(to_host(ef_g), ef_o, what + " ef")
+
+
+def test_hierarchical_qgz_delivers_each_rank_its_partition():
+    """2 nodes x 4 GPUs simulated on one GPU: every rank quantizes its own
+    gradient in ZeRO++'s order, the intra-node all-to-all hands local rank l
+    chunk l of its node peers (8-way... here 4-way reduce + requant), the
+    inter-node all-to-all hands node n sub-chunk n of the same local rank on
+    every node (2-way reduce, alpha 1/8).  Rank r = node*4 + local must end
+    with the average of partition r of all 8 gradients -- bit-exact against
+    the oracle running the same exchanges, and close to the exact mean."""
+    from weight_communication_zero_amd import zeropp_slots
+    intra, inter, B = 4, 2, 128
+    R = intra * inter
+    part = 9 * B * 8  # 9216 elements per partition
+    M = R * part
+    slots = zeropp_slots(intra, inter)
+    grads = [grad_values(M, seed=1000 + r, outlier_p=0.0) for r in range(R)]
+    # every rank: EF int4 quantize into ZeRO++ order
+    cg, sg, co, so = [], [], [], []
+    for r in range(R):
+        c = torch.empty(M // 2, dtype=torch.uint8, device="cuda")
+        s = torch.empty(M // B, dtype=torch.float32, device="cuda")
+        Z().zq_quantize_ef_int4_permuted(to_gpu(grads[r]), None, B, 0.0, 1.0, c, s, slots)
+        c_o, s_o = O.quantize_ef_int4_permuted(grads[r], None, B, 0.0, 1.0, slots)
+        cg.append(c), sg.append(s), co.append(c_o), so.append(s_o)
+    chunk = M // intra  # level-1 chunk: slots [l*inter, (l+1)*inter)
+    l1_g, l1_o = {}, {}
+    for node in range(inter):
+        for l in range(intra):
+            peers = [node * intra + q for q in range(intra)]
+            cc = [cg[p][l * chunk // 2:(l + 1) * chunk // 2] for p in peers]
+            ss = [sg[p][l * chunk // B:(l + 1) * chunk // B] for p in peers]
+            rqc = torch.empty(chunk // 2, dtype=torch.uint8, device="cuda")
+            rqs = torch.empty(chunk // B, dtype=torch.float32, device="cuda")
+            Z().zq_dequant_reduce(cc, ss, chunk, B, 1.0, rq_codes=rqc, rq_scales=rqs)
+            _, rc_o, rs_o = O.dequant_reduce([co[p][l * chunk // 2:(l + 1) * chunk // 2] for p in peers],
+                                             [so[p][l * chunk // B:(l + 1) * chunk // B] for p in peers],
+                                             chunk, B, 1.0, want_out=False, requant=True)
+            l1_g[(node, l)] = (rqc, rqs)
+            l1_o[(node, l)] = (rc_o, rs_o)
+    for node in range(inter):
+        for l in range(intra):
+            r = node * intra + l
+            cc = [l1_g[(nd, l)][0][node * part // 2:(node + 1) * part // 2] for nd in range(inter)]
+            ss = [l1_g[(nd, l)][1][node * part // B:(node + 1) * part // B] for nd in range(inter)]
+            out = torch.empty(part, dtype=torch.float32, device="cuda")
+            Z().zq_dequant_reduce(cc, ss, part, B, 1.0 / R, out=out)
+            out_o, _, _ = O.dequant_reduce(
+                [l1_o[(nd, l)][0][node * part // 2:(node + 1) * part // 2] for nd in range(inter)],
+                [l1_o[(nd, l)][1][node * part // B:(node + 1) * part // B] for nd in range(inter)],
+                part, B, 1.0 / R)
+            torch.cuda.synchronize()
+            got = to_host(out)
+            assert_bits_equal(got, out_o, f"rank {r} final shard")
+            exact = np.mean([g[r * part:(r + 1) * part].astype(np.float64) for g in grads], axis=0)
+            err = np.abs(got - exact)
+            assert np.corrcoef(got, exact)[0, 1] > 0.95, f"rank {r} did not receive partition {r}"
+            assert err.mean() < 0.2 * np.abs(exact).mean(), f"rank {r}: mean error {err.mean()}"

@@ -59,6 +59,46 @@ zq_status zq_quantize_ef_int4(const void* g, zq_dtype g_dtype, float* ef, size_t
                                                 beta_r, codes, scales, (hipStream_t)stream));
 }
 
+zq_status zq_quantize_ef_int4_permuted(const void* g, zq_dtype g_dtype, float* ef, size_t n,
+                                       uint32_t block, float beta_e, float beta_r, uint8_t* codes,
+                                       float* scales, uint32_t n_part,
+                                       const uint32_t* slot_of_part, void* stream) {
+    if (g_dtype != ZQ_FP32 && g_dtype != ZQ_BF16)
+        return ZQ_ERR_DTYPE;
+    if (!valid_block(block))
+        return ZQ_ERR_BLOCK;
+    if (n > kMaxElems || n_part < 1 || n_part > zq::kMaxParts)
+        return ZQ_ERR_SIZE;
+    if (n == 0)
+        return ZQ_OK;
+    if (!g || !codes || !scales || !slot_of_part)
+        return ZQ_ERR_NULL;
+    const size_t part_len = n / n_part;
+    if (part_len * n_part != n || part_len % block || part_len < std::max<size_t>(1024, block))
+        return ZQ_ERR_SIZE;
+    zq::PartPerm perm = {};
+    perm.part_len = part_len;
+    perm.n_part = n_part;
+    bool seen[zq::kMaxParts] = {};
+    for (uint32_t p = 0; p < n_part; ++p) {
+        const uint32_t s = slot_of_part[p];
+        if (s >= n_part || seen[s])
+            return ZQ_ERR_SIZE;
+        seen[s] = true;
+        perm.slot[p] = s;
+    }
+    if (!aligned(g, 16) || !aligned(ef, 16) || !aligned(codes, 16) || !aligned(scales, 4))
+        return ZQ_ERR_ALIGN;
+    const size_t gb = n * (g_dtype == ZQ_BF16 ? 2 : 4), eb = ef ? n * 4 : 0;
+    const size_t cb = zq_int4_code_bytes(n), sb = nblocks(n, block) * 4;
+    if (overlap(codes, cb, g, gb) || overlap(codes, cb, ef, eb) || overlap(codes, cb, scales, sb) ||
+        overlap(scales, sb, g, gb) || overlap(scales, sb, ef, eb) || overlap(ef, eb, g, gb))
+        return ZQ_ERR_ALIAS;
+    return launched(zq::launch_quantize_ef_int4_permuted(g, g_dtype == ZQ_BF16, ef, n, block,
+                                                         beta_e, beta_r, codes, scales, perm,
+                                                         (hipStream_t)stream));
+}
+
 zq_status zq_dequant_reduce(uint32_t P, const uint8_t* const* codes, const float* const* scales,
                             size_t n_chunk, uint32_t block, float alpha, float* out,
                             uint8_t* rq_codes, float* rq_scales, float* rq_ef, float rq_beta_e,

@@ -35,11 +35,35 @@ struct EfqGeom {
     static constexpr int BPT = TILE / B;
 };
 
-template <bool BF16, bool EF, int B, bool MASK>
+// Where the codes and scales of element i go: the same place (plain
+// quantize), or the slot of its partition (permuted quantize).  A tile lies
+// in at most two partitions (partitions are at least a tile long), so the
+// map is the offset of the tile's first partition below `bnd` and of the
+// next one from `bnd` on.
+struct IdentityMap {
+    __device__ __forceinline__ size_t operator()(size_t i) const { return i; }
+};
+
+struct PermMap {
+    size_t bnd;
+    size_t d0, d1;  // added modulo 2^64 (a slot may lie before its partition)
+    __device__ __forceinline__ size_t operator()(size_t i) const { return i + (i < bnd ? d0 : d1); }
+};
+
+__device__ __forceinline__ PermMap perm_map(const PartPerm& pp, size_t base) {
+    const uint32_t p0 = __builtin_amdgcn_readfirstlane((uint32_t)(base / pp.part_len));
+    PermMap m;
+    m.bnd = (size_t)(p0 + 1) * pp.part_len;
+    m.d0 = ((size_t)pp.slot[p0] - p0) * pp.part_len;
+    m.d1 = p0 + 1 < pp.n_part ? ((size_t)pp.slot[p0 + 1] - (p0 + 1)) * pp.part_len : 0;
+    return m;
+}
+
+template <bool BF16, bool EF, int B, bool MASK, class Map = IdentityMap>
 __device__ __forceinline__ void efq_tile(const void* __restrict__ gv, float* __restrict__ ef,
                                          size_t n, float beta_e, float beta_r,
                                          uint8_t* __restrict__ codes, float* __restrict__ scales,
-                                         size_t tile) {
+                                         size_t tile, const Map& out = Map()) {
     using G = EfqGeom<B>;
     const int lane = lane_id();
     const size_t base = tile * (size_t)G::TILE;
@@ -117,7 +141,7 @@ __device__ __forceinline__ void efq_tile(const void* __restrict__ gv, float* __r
             for (int u = 0; u < G::U; ++u) {
                 const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * 4;
                 if (!MASK || i0 < n)
-                    scales[i0 / B] = bs[u].s;
+                    scales[out(i0) / B] = bs[u].s;
             }
         }
     } else {
@@ -126,7 +150,7 @@ __device__ __forceinline__ void efq_tile(const void* __restrict__ gv, float* __r
             for (int b = 0; b < G::BPT; ++b) {
                 const size_t i0 = base + (size_t)b * B;
                 if (!MASK || i0 < n)
-                    scales[i0 / B] = bs[b].s;
+                    scales[out(i0) / B] = bs[b].s;
             }
         }
     }
@@ -160,17 +184,18 @@ __device__ __forceinline__ void efq_tile(const void* __restrict__ gv, float* __r
             if constexpr (EF)
                 e[u][j] = ef_update(c[u][j], k, sc.s, e[u][j], beta_e, beta_r);
         }
+        const size_t o0 = out(i0);
         if constexpr (!MASK) {
-            st_stream((uint16_t)packed, (uint16_t*)(codes + i0 / 2));
+            st_stream((uint16_t)packed, (uint16_t*)(codes + o0 / 2));
             if constexpr (EF) {
                 f4 v = {e[u][0], e[u][1], e[u][2], e[u][3]};
                 st_stream(v, (f4*)(ef + i0));
             }
         } else {
             if (i0 < n)
-                codes[i0 / 2] = (uint8_t)(packed & 0xFFu);
+                codes[o0 / 2] = (uint8_t)(packed & 0xFFu);
             if (i0 + 2 < n)
-                codes[i0 / 2 + 1] = (uint8_t)(packed >> 8);
+                codes[o0 / 2 + 1] = (uint8_t)(packed >> 8);
             if constexpr (EF) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -217,6 +242,61 @@ hipError_t launch_b(const void* g, float* ef, size_t n, float beta_e, float beta
     return e;
 }
 
+template <bool BF16, bool EF, int B, bool MASK>
+__global__ __launch_bounds__(kBlockThreads) void efq_perm_kernel(const void* __restrict__ g,
+                                                                 float* __restrict__ ef, size_t n,
+                                                                 float beta_e, float beta_r,
+                                                                 uint8_t* __restrict__ codes,
+                                                                 float* __restrict__ scales,
+                                                                 PartPerm perm) {
+    using G = EfqGeom<B>;
+    if constexpr (MASK) {
+        const size_t t = n / G::TILE;
+        efq_tile<BF16, EF, B, true>(g, ef, n, beta_e, beta_r, codes, scales, t,
+                                    perm_map(perm, t * G::TILE));
+    } else {
+        const size_t nfull = n / G::TILE;
+        for (size_t t = wave_id(); t < nfull; t += wave_count())
+            efq_tile<BF16, EF, B, false>(g, ef, n, beta_e, beta_r, codes, scales, t,
+                                         perm_map(perm, t * G::TILE));
+    }
+}
+
+template <bool BF16, bool EF, int B>
+hipError_t launch_perm_b(const void* g, float* ef, size_t n, float beta_e, float beta_r,
+                         uint8_t* codes, float* scales, const PartPerm& perm, hipStream_t stream) {
+    using G = EfqGeom<B>;
+    const size_t nfull = n / G::TILE;
+    PartPerm arg = perm;
+    void* args[] = {(void*)&g, (void*)&ef, (void*)&n, (void*)&beta_e, (void*)&beta_r,
+                    (void*)&codes, (void*)&scales, (void*)&arg};
+    hipError_t e = hipSuccess;
+    if (nfull)
+        e = hipLaunchKernel((const void*)&efq_perm_kernel<BF16, EF, B, false>,
+                            grid_for_tiles(nfull, kGeomStream), dim3(kGeomStream.threads), args, 0,
+                            stream);
+    if (e == hipSuccess && n % G::TILE)
+        e = hipLaunchKernel((const void*)&efq_perm_kernel<BF16, EF, B, true>, dim3(1),
+                            dim3(kWave), args, 0, stream);
+    return e;
+}
+
+template <bool BF16, bool EF>
+hipError_t launch_perm_t(const void* g, float* ef, size_t n, uint32_t block, float be, float br,
+                         uint8_t* codes, float* scales, const PartPerm& pp, hipStream_t st) {
+    switch (block) {
+        case 32: return launch_perm_b<BF16, EF, 32>(g, ef, n, be, br, codes, scales, pp, st);
+        case 64: return launch_perm_b<BF16, EF, 64>(g, ef, n, be, br, codes, scales, pp, st);
+        case 128: return launch_perm_b<BF16, EF, 128>(g, ef, n, be, br, codes, scales, pp, st);
+        case 256: return launch_perm_b<BF16, EF, 256>(g, ef, n, be, br, codes, scales, pp, st);
+        case 512: return launch_perm_b<BF16, EF, 512>(g, ef, n, be, br, codes, scales, pp, st);
+        case 1024: return launch_perm_b<BF16, EF, 1024>(g, ef, n, be, br, codes, scales, pp, st);
+        case 2048: return launch_perm_b<BF16, EF, 2048>(g, ef, n, be, br, codes, scales, pp, st);
+        case 4096: return launch_perm_b<BF16, EF, 4096>(g, ef, n, be, br, codes, scales, pp, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <bool BF16, bool EF>
 hipError_t launch_t(const void* g, float* ef, size_t n, uint32_t block, float be, float br,
                     uint8_t* codes, float* scales, hipStream_t st) {
@@ -243,6 +323,21 @@ hipError_t launch_quantize_ef_int4(const void* g, bool g_bf16, float* ef, size_t
                   : launch_t<true, false>(g, ef, n, block, beta_e, beta_r, codes, scales, stream);
     return ef ? launch_t<false, true>(g, ef, n, block, beta_e, beta_r, codes, scales, stream)
               : launch_t<false, false>(g, ef, n, block, beta_e, beta_r, codes, scales, stream);
+}
+
+hipError_t launch_quantize_ef_int4_permuted(const void* g, bool g_bf16, float* ef, size_t n,
+                                            uint32_t block, float beta_e, float beta_r,
+                                            uint8_t* codes, float* scales, const PartPerm& perm,
+                                            hipStream_t stream) {
+    if (g_bf16)
+        return ef ? launch_perm_t<true, true>(g, ef, n, block, beta_e, beta_r, codes, scales, perm,
+                                              stream)
+                  : launch_perm_t<true, false>(g, ef, n, block, beta_e, beta_r, codes, scales,
+                                               perm, stream);
+    return ef ? launch_perm_t<false, true>(g, ef, n, block, beta_e, beta_r, codes, scales, perm,
+                                           stream)
+              : launch_perm_t<false, false>(g, ef, n, block, beta_e, beta_r, codes, scales, perm,
+                                            stream);
 }
 
 }  // namespace zq

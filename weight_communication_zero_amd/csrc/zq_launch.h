@@ -53,6 +53,20 @@ hipError_t launch_quantize_ef_int4(const void* g, bool g_bf16, float* ef, size_t
                                    float beta_e, float beta_r, uint8_t* codes, float* scales,
                                    hipStream_t stream);
 
+// Partition permutation of the EF quantizer's outputs (codes and scales of
+// partition p go to slot slot[p]).
+constexpr uint32_t kMaxParts = 256;
+struct PartPerm {
+    uint64_t part_len;
+    uint32_t n_part;
+    uint32_t slot[kMaxParts];
+};
+
+hipError_t launch_quantize_ef_int4_permuted(const void* g, bool g_bf16, float* ef, size_t n,
+                                            uint32_t block, float beta_e, float beta_r,
+                                            uint8_t* codes, float* scales, const PartPerm& perm,
+                                            hipStream_t stream);
+
 struct DrParams {
     const uint8_t* codes[kMaxPeers];
     const float* scales[kMaxPeers];

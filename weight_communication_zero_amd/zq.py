@@ -58,6 +58,9 @@ def _load() -> C.CDLL:
     for f in ("zq_quantize_ef_int4", "zq_dequant_reduce", "zq_quant_int8", "zq_dequant_int8",
               "zq_sr_accumulate"):
         getattr(L, f).restype = i32
+    L.zq_quantize_ef_int4_permuted.argtypes = [vp, i32, vp, sz, u32, f32, f32, vp, vp, u32, vp,
+                                               vp]
+    L.zq_quantize_ef_int4_permuted.restype = i32
     L.zq_sr_accumulate_batched.argtypes = [vp, u32, i32, vp]
     L.zq_sr_accumulate_batched.restype = i32
     L.zq_int4_code_bytes.argtypes = [sz]
@@ -158,6 +161,31 @@ def zq_quantize_ef_int4(g, ef, block: int, beta_e: float, beta_r: float, codes, 
     _check("zq_quantize_ef_int4",
            lib.zq_quantize_ef_int4(_p(g), _dtype(g), _p(ef), n, block, beta_e, beta_r, _p(codes),
                                    _p(scales), _stream(stream)))
+
+
+def zeropp_slots(intra: int, inter: int) -> list[int]:
+    """ZeRO++'s partition order for `inter` nodes of `intra` GPUs: rank
+    r = node * intra + local owns partition r, which must sit in slot
+    local * inter + node for the intra-node then inter-node all-to-alls to
+    deliver it to rank r."""
+    return [(r % intra) * inter + r // intra for r in range(intra * inter)]
+
+
+def zq_quantize_ef_int4_permuted(g, ef, block: int, beta_e: float, beta_r: float, codes, scales,
+                                 slot_of_part, stream=None, n: int | None = None) -> None:
+    """EF int4 quantize whose codes / scales of partition p land in slot
+    slot_of_part[p] (g and ef stay in natural order)."""
+    n = g.numel() if n is None else n
+    nb = (n + block - 1) // block if block > 0 else 0
+    _need("g", g, n, _FLOAT)
+    _need("ef", ef, n, _F32)
+    _need("codes", codes, (n + 1) // 2, _U8)
+    _need("scales", scales, nb, _F32)
+    slots = (C.c_uint32 * max(len(slot_of_part), 1))(*slot_of_part)
+    _check("zq_quantize_ef_int4_permuted",
+           lib.zq_quantize_ef_int4_permuted(_p(g), _dtype(g), _p(ef), n, block, beta_e, beta_r,
+                                            _p(codes), _p(scales), len(slot_of_part),
+                                            C.cast(slots, C.c_void_p), _stream(stream)))
 
 
 def zq_dequant_reduce(codes_list, scales_list, n_chunk: int, block: int, alpha: float, out=None,
