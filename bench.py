@@ -212,7 +212,17 @@ def main():
     slots = zq.zeropp_slots(P1, P2)
     ms_perm = timed(torch, lambda: zq.zq_quantize_ef_int4_permuted(g, ef, B, beta, 1.0, codes,
                                                                    scales, slots), 10)
+    # DeepSpeed-style per-parameter quantize: the 327 tensors, one batched call
+    segs, off = [], 0
+    for t in tensors:
+        segs.append((g[off:off + t.numel], ef[off:off + t.numel],
+                     codes[off // 2:(off + t.numel) // 2], scales[off // B:(off + t.numel) // B]))
+        off += t.numel
+    table = zq.EfqSegmentTable(segs, B)
+    ms_batched = timed(torch, lambda: zq.zq_quantize_ef_int4_batched(table, B, beta, 1.0), 10)
+    del segs, table
     rows = {
+        "efq_batched_327_tensors_fp32_b128_7.5B": row(bytes_efq, ms_batched, M),
         "efq_permuted_zeropp_4x8_fp32_b128_7.5B": row(bytes_efq, ms_perm, M),
         "dequant_reduce_requant_ef_p8_b128_7.5B": row(
             dr_bytes(n1, B, P1, out=False, rq=True, rq_ef=True), ms_rqef, n1),

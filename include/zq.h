@@ -125,6 +125,34 @@ zq_status zq_quantize_ef_int4_permuted(const void *g, zq_dtype g_dtype, float *e
                                        const uint32_t *slot_of_part, void *stream);
 
 /*
+ * zq_quantize_ef_int4_batched -- zq_quantize_ef_int4 over many tensors in one
+ * call: DeepSpeed's LoCo path quantizes parameter by parameter, each with
+ * its own error-feedback buffer ([LoCo] review thread: the EF buffer kept on
+ * each parameter, p.inter_ef_buf); here one pass covers all of them, up to
+ * 32 tensors per kernel launch (the table travels in the kernel arguments;
+ * nothing is allocated).
+ *
+ * Segment i is exactly zq_quantize_ef_int4(seg.g, g_dtype, seg.ef, seg.n,
+ * block, beta_e, beta_r, seg.codes, seg.scales): blocks restart at every
+ * segment and a segment's last block may be partial.
+ *   segs   HOST array of n_seg segments; every pointer 16-byte aligned (scales
+ *          4-byte); ef is NULL in all segments or in none (ZQ_ERR_NULL).
+ * Errors: as zq_quantize_ef_int4 per segment; ZQ_ERR_SIZE for n_seg > 65536
+ * or a segment longer than 2^40 elements; ZQ_ERR_ALIAS when any output (or
+ * EF buffer) overlaps any other range of any segment.
+ */
+typedef struct {
+    const void *g;
+    float *ef;
+    uint8_t *codes;
+    float *scales;
+    uint64_t n;
+} zq_efq_segment;
+
+zq_status zq_quantize_ef_int4_batched(const zq_efq_segment *segs, uint32_t n_seg, zq_dtype g_dtype,
+                                      uint32_t block, float beta_e, float beta_r, void *stream);
+
+/*
  * zq_dequant_reduce -- qgZ receive side: dequantize the P int4 chunks an
  * all-to-all delivers to this GPU and reduce them in full precision, with an
  * optional requantization for the next level of the hierarchy ([ZeRO++]

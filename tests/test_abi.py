@@ -17,6 +17,7 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails va
 def test_exports_every_declared_symbol():
     names = zq.declared_symbols()
     assert set(names) == {"zq_quantize_ef_int4", "zq_quantize_ef_int4_permuted",
+                          "zq_quantize_ef_int4_batched",
                           "zq_dequant_reduce", "zq_quant_int8",
                           "zq_dequant_int8", "zq_sr_accumulate", "zq_sr_accumulate_batched",
                           "zq_int4_code_bytes",
@@ -177,3 +178,31 @@ def test_permuted_quantize_validation():
     assert call(codes=FAKE + 0x1000002) == zq.ZQ_ERR_ALIGN
     assert call(codes=FAKE + 0x100) == zq.ZQ_ERR_ALIAS
     assert zq.zeropp_slots(4, 2) == [0, 2, 4, 6, 1, 3, 5, 7]
+
+
+def test_efq_batched_validation():
+    Seg = zq.EfqSegment
+
+    def call(segs, dt=0, block=128, n_seg=None):
+        arr = (Seg * max(len(segs), 1))(*segs)
+        return L.zq_quantize_ef_int4_batched(C.cast(arr, C.c_void_p),
+                                             len(segs) if n_seg is None else n_seg, dt, block, 1.0,
+                                             1.0, None)
+
+    def seg(base, n=4096, ef=True):
+        return Seg(base, base + 0x100000 if ef else None, base + 0x200000, base + 0x300000, n)
+
+    a, b = seg(FAKE), seg(FAKE + 0x1000000)
+    assert call([a], dt=3) == zq.ZQ_ERR_DTYPE
+    assert call([a], block=33) == zq.ZQ_ERR_BLOCK
+    assert L.zq_quantize_ef_int4_batched(None, 0, 0, 128, 1.0, 1.0, None) == zq.ZQ_OK
+    assert L.zq_quantize_ef_int4_batched(None, 2, 0, 128, 1.0, 1.0, None) == zq.ZQ_ERR_NULL
+    assert call([a], n_seg=70000) == zq.ZQ_ERR_SIZE
+    assert call([seg(FAKE, n=(1 << 40) + 1)]) == zq.ZQ_ERR_SIZE
+    assert call([a, seg(FAKE + 0x1000000, ef=False)]) == zq.ZQ_ERR_NULL  # EF in some, not all
+    assert call([Seg(FAKE, None, None, FAKE + 0x300000, 4096)]) == zq.ZQ_ERR_NULL
+    assert call([Seg(FAKE + 8, None, FAKE + 0x200000, FAKE + 0x300000, 4096)]) == zq.ZQ_ERR_ALIGN
+    assert call([a, seg(FAKE + 0x100)]) == zq.ZQ_ERR_ALIAS  # b's g inside a's g? no: outputs overlap
+    assert call([a, Seg(FAKE + 0x10000, FAKE + 0x1100000, FAKE + 0x200100, FAKE + 0x1300000, 64)]) \
+        == zq.ZQ_ERR_ALIAS  # codes overlap
+    assert call([Seg(FAKE, None, FAKE + 0x200000, FAKE + 0x300000, 0)]) == zq.ZQ_OK  # all empty

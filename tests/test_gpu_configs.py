@@ -310,3 +310,37 @@ def test_gpt2_per_tensor_zero2_batched():
     segs = gpt2_segments(grads, shards, tensors, rank, P, 0)
     for i in pick:
         assert_bits_equal(to_host(segs[i][0]), exp[i], f"tensor {i} ({tensors[i].name}) shard")
+
+
+def test_per_tensor_batched_quantize_equals_flat_call_0p85b():
+    """DeepSpeed-style per-parameter EF quantize of the 129 tensors of the
+    ~0.85B model in one batched call equals the flat call over the same
+    buffer bit for bit (every tensor is whole 128-element blocks), over 3 steps
+    of EF evolution."""
+    tensors = synth.llama_0p85b()
+    M = synth.total(tensors)
+    B = 128
+    g = torch.empty(M, dtype=torch.float32, device="cuda")
+    ef_a = torch.zeros(M, dtype=torch.float32, device="cuda")
+    ef_b = torch.zeros(M, dtype=torch.float32, device="cuda")
+    ca = torch.empty(M // 2, dtype=torch.uint8, device="cuda")
+    cb = torch.empty(M // 2, dtype=torch.uint8, device="cuda")
+    sa = torch.empty(M // B, dtype=torch.float32, device="cuda")
+    sb = torch.empty(M // B, dtype=torch.float32, device="cuda")
+    segs, off = [], 0
+    for t in tensors:
+        n = t.numel
+        segs.append((g[off:off + n], ef_b[off:off + n], cb[off // 2:(off + n) // 2],
+                     sb[off // B:(off + n) // B]))
+        off += n
+    from weight_communication_zero_amd import EfqSegmentTable
+    table = EfqSegmentTable(segs, B)
+    for step in range(3):
+        synth.fill_model(g, tensors, std=1e-3, seed=synth.seed_for("llama0p85b", "grad", step=step),
+                         heavy_tails=True)
+        Z().zq_quantize_ef_int4(g, ef_a, B, 0.9, 1.0, ca, sa)
+        Z().zq_quantize_ef_int4_batched(table, B, 0.9, 1.0)
+        torch.cuda.synchronize()
+        assert torch.equal(ca, cb), f"step {step} codes"
+        assert torch.equal(sa.view(torch.int32), sb.view(torch.int32)), f"step {step} scales"
+        assert torch.equal(ef_a.view(torch.int32), ef_b.view(torch.int32)), f"step {step} ef"

@@ -454,3 +454,35 @@ def test_hierarchical_qgz_delivers_each_rank_its_partition():
             err = np.abs(got - exact)
             assert np.corrcoef(got, exact)[0, 1] > 0.95, f"rank {r} did not receive partition {r}"
             assert err.mean() < 0.2 * np.abs(exact).mean(), f"rank {r}: mean error {err.mean()}"
+
+
+# ------------------------------------------------- batched EF quantize --
+
+@pytest.mark.parametrize("block", [128, 256, 2048])
+@pytest.mark.parametrize("gdt", ["fp32", "bf16"])
+@pytest.mark.parametrize("with_ef", [False, True])
+def test_efq_batched_matches_oracle(block, gdt, with_ef):
+    """45 tensors (two launches of at most 32 plus their tail launches),
+    ragged lengths from 1 element to several tiles."""
+    rng = np.random.default_rng(block * 7 + (gdt == "bf16") * 3 + with_ef)
+    segs_g, exp = [], []
+    for i in range(45):
+        n = int(rng.choice([1, 3, block - 1, block, 1024, 4096, 4096 + 17, 3 * max(1024, block) + 5,
+                            20000]))
+        x = grad_values(n, seed=300 + i, special=True, block=block)
+        g = as_bf16_bits(x) if gdt == "bf16" else x
+        ef_h = grad_values(n, seed=900 + i, std=1e-5) if with_ef else None
+        ef_o = ef_h.copy() if with_ef else None
+        c_o, s_o = O.quantize_ef_int4(g, ef_o, block, 0.9, 1.0)
+        exp.append((c_o, s_o, ef_o))
+        codes = Guarded((n + 1) // 2, torch.uint8)
+        scales = Guarded(-(-n // block), torch.float32)
+        segs_g.append((to_gpu(g), to_gpu(ef_h) if with_ef else None, codes, scales))
+    Z().zq_quantize_ef_int4_batched([(g, e, c.t, s.t) for g, e, c, s in segs_g], block, 0.9, 1.0)
+    torch.cuda.synchronize()
+    for i, ((g, e, c, s), (c_o, s_o, ef_o)) in enumerate(zip(segs_g, exp)):
+        what = f"batched efq segment {i} n={g.numel()} B={block} {gdt} ef={with_ef}"
+        assert_bits_equal(c.host(), c_o, what + " codes")
+        assert_bits_equal(s.host(), s_o, what + " scales")
+        if with_ef:
+            assert_bits_equal(to_host(e), ef_o, what + " ef")

@@ -99,6 +99,68 @@ zq_status zq_quantize_ef_int4_permuted(const void* g, zq_dtype g_dtype, float* e
                                                          (hipStream_t)stream));
 }
 
+zq_status zq_quantize_ef_int4_batched(const zq_efq_segment* segs, uint32_t n_seg,
+                                      zq_dtype g_dtype, uint32_t block, float beta_e,
+                                      float beta_r, void* stream) {
+    if (g_dtype != ZQ_FP32 && g_dtype != ZQ_BF16)
+        return ZQ_ERR_DTYPE;
+    if (!valid_block(block))
+        return ZQ_ERR_BLOCK;
+    if (n_seg == 0)
+        return ZQ_OK;
+    if (!segs)
+        return ZQ_ERR_NULL;
+    if (n_seg > 65536)
+        return ZQ_ERR_SIZE;
+    struct Range {
+        uintptr_t lo, hi;
+        bool written;
+    };
+    std::vector<Range> ranges;
+    std::vector<zq::EfqSegment> dev;
+    ranges.reserve(4 * (size_t)n_seg);
+    dev.reserve(n_seg);
+    int ef_state = -1;  // unknown / 0 none / 1 all
+    const size_t esz = g_dtype == ZQ_BF16 ? 2 : 4;
+    for (uint32_t i = 0; i < n_seg; ++i) {
+        const zq_efq_segment& s = segs[i];
+        if (s.n > kMaxSegElems)
+            return ZQ_ERR_SIZE;
+        if (s.n == 0)
+            continue;
+        if (!s.g || !s.codes || !s.scales)
+            return ZQ_ERR_NULL;
+        const int has_ef = s.ef ? 1 : 0;
+        if (ef_state >= 0 && has_ef != ef_state)
+            return ZQ_ERR_NULL;
+        ef_state = has_ef;
+        if (!aligned(s.g, 16) || !aligned(s.ef, 16) || !aligned(s.codes, 16) ||
+            !aligned(s.scales, 4))
+            return ZQ_ERR_ALIGN;
+        ranges.push_back({(uintptr_t)s.g, (uintptr_t)s.g + esz * s.n, false});
+        if (s.ef)
+            ranges.push_back({(uintptr_t)s.ef, (uintptr_t)s.ef + 4 * s.n, true});
+        ranges.push_back({(uintptr_t)s.codes, (uintptr_t)s.codes + zq_int4_code_bytes(s.n), true});
+        ranges.push_back({(uintptr_t)s.scales, (uintptr_t)s.scales + 4 * nblocks(s.n, block), true});
+        dev.push_back({s.g, s.ef, s.codes, s.scales, s.n});
+    }
+    if (dev.empty())
+        return ZQ_OK;
+    std::sort(ranges.begin(), ranges.end(),
+              [](const Range& a, const Range& b) { return a.lo < b.lo; });
+    uintptr_t max_end_any = 0, max_end_written = 0;
+    for (const Range& r : ranges) {
+        if (r.lo < (r.written ? max_end_any : max_end_written))
+            return ZQ_ERR_ALIAS;
+        max_end_any = std::max(max_end_any, r.hi);
+        if (r.written)
+            max_end_written = std::max(max_end_written, r.hi);
+    }
+    return launched(zq::launch_quantize_ef_int4_batched(dev.data(), (uint32_t)dev.size(),
+                                                        g_dtype == ZQ_BF16, ef_state == 1, block,
+                                                        beta_e, beta_r, (hipStream_t)stream));
+}
+
 zq_status zq_dequant_reduce(uint32_t P, const uint8_t* const* codes, const float* const* scales,
                             size_t n_chunk, uint32_t block, float alpha, float* out,
                             uint8_t* rq_codes, float* rq_scales, float* rq_ef, float rq_beta_e,

@@ -297,6 +297,96 @@ hipError_t launch_perm_t(const void* g, float* ef, size_t n, uint32_t block, flo
     }
 }
 
+// Batched segments.  The main launch runs the full tiles of up to kEfqSegs
+// segments; a second launch runs every segment's ragged last tile (masked),
+// one wave each.  A wave finds its segment by binary search over the
+// cumulative tile counts in the kernel arguments (five scalar loads).
+constexpr int kEfqSegs = 32;
+
+struct EfqBatch {
+    EfqSegment seg[kEfqSegs];
+    uint32_t tile_end[kEfqSegs];  // cumulative tiles through segment s
+    uint32_t nseg;
+    uint32_t total;
+    float beta_e, beta_r;
+};
+
+__device__ __forceinline__ uint32_t find_segment(const EfqBatch& b, uint32_t t) {
+    uint32_t lo = 0, hi = b.nseg - 1;  // first s with t < tile_end[s]
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (t < b.tile_end[mid])
+            hi = mid;
+        else
+            lo = mid + 1;
+    }
+    return lo;
+}
+
+template <bool BF16, bool EF, int B, bool MASK>
+__global__ __launch_bounds__(kBlockThreads) void efq_batched_kernel(EfqBatch b) {
+    using G = EfqGeom<B>;
+    for (size_t ts = wave_id(); ts < b.total; ts += wave_count()) {
+        const uint32_t t = (uint32_t)ts;
+        const uint32_t s = find_segment(b, t);
+        const EfqSegment& g = b.seg[s];
+        // full tiles: local index within the segment; tails: the segment's last tile
+        const size_t local = MASK ? g.n / G::TILE : t - (s ? b.tile_end[s - 1] : 0u);
+        efq_tile<BF16, EF, B, MASK>(g.g, g.ef, g.n, b.beta_e, b.beta_r, g.codes, g.scales, local);
+    }
+}
+
+template <bool BF16, bool EF, int B>
+hipError_t launch_batched_b(const EfqSegment* segs, uint32_t n_seg, float be, float br,
+                            hipStream_t stream) {
+    using G = EfqGeom<B>;
+    for (int pass = 0; pass < 2; ++pass) {  // 0: full tiles, 1: ragged last tiles
+        uint32_t i = 0;
+        while (i < n_seg) {
+            EfqBatch bt = {};
+            bt.beta_e = be;
+            bt.beta_r = br;
+            uint64_t tiles = 0;
+            while (i < n_seg && bt.nseg < (uint32_t)kEfqSegs) {
+                const EfqSegment& g = segs[i++];
+                const uint64_t t = pass == 0 ? g.n / G::TILE : (g.n % G::TILE ? 1 : 0);
+                if (t == 0)
+                    continue;
+                bt.seg[bt.nseg] = g;
+                tiles += t;
+                bt.tile_end[bt.nseg++] = (uint32_t)tiles;
+            }
+            if (bt.nseg == 0)
+                continue;
+            bt.total = (uint32_t)tiles;
+            void* args[] = {(void*)&bt};
+            const void* fn = pass == 0 ? (const void*)&efq_batched_kernel<BF16, EF, B, false>
+                                       : (const void*)&efq_batched_kernel<BF16, EF, B, true>;
+            const hipError_t e = hipLaunchKernel(fn, grid_for_tiles(tiles, kGeomStream),
+                                                 dim3(kGeomStream.threads), args, 0, stream);
+            if (e != hipSuccess)
+                return e;
+        }
+    }
+    return hipSuccess;
+}
+
+template <bool BF16, bool EF>
+hipError_t launch_batched_t(const EfqSegment* segs, uint32_t n_seg, uint32_t block, float be,
+                            float br, hipStream_t st) {
+    switch (block) {
+        case 32: return launch_batched_b<BF16, EF, 32>(segs, n_seg, be, br, st);
+        case 64: return launch_batched_b<BF16, EF, 64>(segs, n_seg, be, br, st);
+        case 128: return launch_batched_b<BF16, EF, 128>(segs, n_seg, be, br, st);
+        case 256: return launch_batched_b<BF16, EF, 256>(segs, n_seg, be, br, st);
+        case 512: return launch_batched_b<BF16, EF, 512>(segs, n_seg, be, br, st);
+        case 1024: return launch_batched_b<BF16, EF, 1024>(segs, n_seg, be, br, st);
+        case 2048: return launch_batched_b<BF16, EF, 2048>(segs, n_seg, be, br, st);
+        case 4096: return launch_batched_b<BF16, EF, 4096>(segs, n_seg, be, br, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <bool BF16, bool EF>
 hipError_t launch_t(const void* g, float* ef, size_t n, uint32_t block, float be, float br,
                     uint8_t* codes, float* scales, hipStream_t st) {
@@ -323,6 +413,16 @@ hipError_t launch_quantize_ef_int4(const void* g, bool g_bf16, float* ef, size_t
                   : launch_t<true, false>(g, ef, n, block, beta_e, beta_r, codes, scales, stream);
     return ef ? launch_t<false, true>(g, ef, n, block, beta_e, beta_r, codes, scales, stream)
               : launch_t<false, false>(g, ef, n, block, beta_e, beta_r, codes, scales, stream);
+}
+
+hipError_t launch_quantize_ef_int4_batched(const EfqSegment* segs, uint32_t n_seg, bool g_bf16,
+                                           bool with_ef, uint32_t block, float beta_e,
+                                           float beta_r, hipStream_t stream) {
+    if (g_bf16)
+        return with_ef ? launch_batched_t<true, true>(segs, n_seg, block, beta_e, beta_r, stream)
+                       : launch_batched_t<true, false>(segs, n_seg, block, beta_e, beta_r, stream);
+    return with_ef ? launch_batched_t<false, true>(segs, n_seg, block, beta_e, beta_r, stream)
+                   : launch_batched_t<false, false>(segs, n_seg, block, beta_e, beta_r, stream);
 }
 
 hipError_t launch_quantize_ef_int4_permuted(const void* g, bool g_bf16, float* ef, size_t n,

@@ -67,6 +67,19 @@ hipError_t launch_quantize_ef_int4_permuted(const void* g, bool g_bf16, float* e
                                             uint8_t* codes, float* scales, const PartPerm& perm,
                                             hipStream_t stream);
 
+// One tensor of a batched EF quantize (validated by the ABI layer).
+struct EfqSegment {
+    const void* g;
+    float* ef;
+    uint8_t* codes;
+    float* scales;
+    uint64_t n;
+};
+
+hipError_t launch_quantize_ef_int4_batched(const EfqSegment* segs, uint32_t n_seg, bool g_bf16,
+                                           bool with_ef, uint32_t block, float beta_e,
+                                           float beta_r, hipStream_t stream);
+
 struct DrParams {
     const uint8_t* codes[kMaxPeers];
     const float* scales[kMaxPeers];

@@ -37,6 +37,12 @@ class SrSegment(C.Structure):
                 ("counter_base", C.c_uint64)]
 
 
+class EfqSegment(C.Structure):
+    """zq_efq_segment of include/zq.h."""
+    _fields_ = [("g", C.c_void_p), ("ef", C.c_void_p), ("codes", C.c_void_p),
+                ("scales", C.c_void_p), ("n", C.c_uint64)]
+
+
 class ZQError(RuntimeError):
     def __init__(self, fn: str, status: int):
         super().__init__(f"{fn} failed: {lib.zq_status_str(status).decode()}")
@@ -61,6 +67,8 @@ def _load() -> C.CDLL:
     L.zq_quantize_ef_int4_permuted.argtypes = [vp, i32, vp, sz, u32, f32, f32, vp, vp, u32, vp,
                                                vp]
     L.zq_quantize_ef_int4_permuted.restype = i32
+    L.zq_quantize_ef_int4_batched.argtypes = [vp, u32, i32, u32, f32, f32, vp]
+    L.zq_quantize_ef_int4_batched.restype = i32
     L.zq_sr_accumulate_batched.argtypes = [vp, u32, i32, vp]
     L.zq_sr_accumulate_batched.restype = i32
     L.zq_int4_code_bytes.argtypes = [sz]
@@ -267,3 +275,37 @@ def zq_sr_accumulate_batched(segments, zero_src: bool = False, stream=None) -> N
     _check("zq_sr_accumulate_batched",
            lib.zq_sr_accumulate_batched(table.ptr, len(table.segments), 1 if zero_src else 0,
                                         _stream(stream)))
+
+
+class EfqSegmentTable:
+    """A marshalled segment table for zq_quantize_ef_int4_batched: tuples
+    (g, ef or None, codes, scales) of per-tensor buffers (n = g.numel())."""
+
+    def __init__(self, segments, block: int):
+        self.segments = list(segments)
+        self.arr = (EfqSegment * max(len(self.segments), 1))()
+        self.dtype = None
+        for i, (g, ef, codes, scales) in enumerate(self.segments):
+            n = g.numel()
+            _need("g", g, n, _FLOAT)
+            _need("ef", ef, n, _F32)
+            _need("codes", codes, (n + 1) // 2, _U8)
+            _need("scales", scales, (n + block - 1) // block, _F32)
+            dt = _dtype(g)
+            if self.dtype is not None and dt != self.dtype:
+                raise TypeError("all segments of a batch share one gradient dtype")
+            self.dtype = dt
+            self.arr[i] = EfqSegment(_p(g), _p(ef), _p(codes), _p(scales), n)
+        self.block = block
+        self.ptr = C.cast(self.arr, C.c_void_p)
+
+
+def zq_quantize_ef_int4_batched(segments, block: int, beta_e: float, beta_r: float,
+                                stream=None) -> None:
+    """Per-tensor EF int4 quantize of many tensors in one call: `segments` is
+    an EfqSegmentTable or an iterable of (g, ef or None, codes, scales)."""
+    table = segments if isinstance(segments, EfqSegmentTable) else EfqSegmentTable(segments, block)
+    _check("zq_quantize_ef_int4_batched",
+           lib.zq_quantize_ef_int4_batched(table.ptr, len(table.segments),
+                                           ZQ_FP32 if table.dtype is None else table.dtype, block,
+                                           beta_e, beta_r, _stream(stream)))
