@@ -304,6 +304,21 @@ def row(nbytes, ms, elems):
             "Gelem/s": round(elems / (ms * 1e-3) / 1e9, 3), "bytes": nbytes}
 
 
+# The sources that define each profiled kernel: its counter summary stays
+# valid while these files are unchanged.
+KERNEL_SOURCES = {"efq_fp32_b128": ("zq_device.h", "zq_launch.h", "zq_efq.hip")}
+
+
+def kernel_source_hash(kernel_tag):
+    import hashlib
+    src = os.path.join(ROOT, "weight_communication_zero_amd", "csrc")
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel_tag]:
+        with open(os.path.join(src, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def measured_traffic(kernel_tag, algorithmic_bytes):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
     this kernel, if its recorded source hash matches the current kernel
@@ -314,11 +329,11 @@ def measured_traffic(kernel_tag, algorithmic_bytes):
     if not os.path.exists(path):
         return None
     h = hashlib.sha256()
-    for f in sorted(os.listdir(src)):
+    for f in KERNEL_SOURCES[kernel_tag]:
         with open(os.path.join(src, f), "rb") as fh:
             h.update(fh.read())
     text = open(path).read()
-    m_hash = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    m_hash = re.search(r"source_sha256[^:\n]*:\s*([0-9a-f]{64})", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m_hash or not m_bytes or m_hash.group(1) != h.hexdigest():
         return None
