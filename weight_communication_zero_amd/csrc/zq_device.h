@@ -70,16 +70,18 @@ __device__ __forceinline__ uint32_t absbits(float x) { return fbits(x) & 0x7FFFF
 // quad_perm swaps (xor 1, xor 2), row half-mirror (pairs quads within 8),
 // row mirror (pairs half-rows within 16), ds_swizzle xor 16 (within 32), and
 // gfx950's v_permlane32_swap (exchanges the two 32-lane halves).
+// The DPP steps are written with bound_ctrl and an identity (0) old value,
+// so the compiler fuses each move into the maximum (v_max_u32_dpp).
 template <int G>
 __device__ __forceinline__ uint32_t group_max(uint32_t v) {
     if constexpr (G >= 2)
-        v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
+        v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true));
     if constexpr (G >= 4)
-        v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
+        v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true));
     if constexpr (G >= 8)
-        v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));
+        v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, true));
     if constexpr (G >= 16)
-        v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));
+        v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, true));
     if constexpr (G >= 32)
         v = max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));
     if constexpr (G >= 64) {

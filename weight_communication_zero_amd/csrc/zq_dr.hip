@@ -15,6 +15,8 @@
 // reads 256 contiguous bytes.  The sum order is fixed (ascending peer), so
 // the fp32 sums -- and the requant codes that depend on their exact bits --
 // are deterministic.  No LDS.
+#include <type_traits>
+
 #include "zq_device.h"
 #include "zq_launch.h"
 
@@ -25,16 +27,34 @@
 namespace zq {
 namespace {
 
-template <int B>
+// VEC outputs per lane per sub-vector: 8 (one 32-bit code word per peer,
+// two 16-byte output stores per lane) or 4 (one 16-bit code word per peer,
+// one 16-byte store per lane, so each store instruction writes 1 KB
+// contiguously).  Both keep 16 outputs per lane per tile.
+#ifndef ZQ_DR_VEC_OUT
+#define ZQ_DR_VEC_OUT 4
+#endif
+#ifndef ZQ_DR_VEC_RQ
+#define ZQ_DR_VEC_RQ 8
+#endif
+
+template <int B, int V>
 struct DrGeom {
-    static constexpr int VEC = 8;
+    static constexpr int VEC = V;
     static constexpr int SUB = kWave * VEC;
     static constexpr int LPB = B <= SUB ? B / VEC : kWave;
     static constexpr int SPB = B <= SUB ? 1 : B / SUB;
-    static constexpr int U = SPB > ZQ_DR_U ? SPB : ZQ_DR_U;
+    static constexpr int U0 = ZQ_DR_U * 8 / VEC;
+    static constexpr int U = SPB > U0 ? SPB : U0;
     static constexpr int TILE = SUB * U;
     static constexpr int BPT = TILE / B;
 };
+
+template <bool RQ>
+constexpr int dr_vec() { return RQ ? ZQ_DR_VEC_RQ : ZQ_DR_VEC_OUT; }
+
+template <int V>
+using code_word_t = typename std::conditional<V == 8, uint32_t, uint16_t>::type;
 
 // Signed value of nibble j of a code word (shift it to the top, then an
 // arithmetic shift back down sign-extends it).
@@ -42,12 +62,13 @@ __device__ __forceinline__ float nib(uint32_t w, int j) {
     return (float)((int32_t)(w << (28 - 4 * j)) >> 28);
 }
 
-// Up to 4 code bytes starting at byte offset ob, only those below nbytes.
+// Up to NB code bytes starting at byte offset ob, only those below nbytes.
+template <int NB>
 __device__ __forceinline__ uint32_t load_code_word_masked(const uint8_t* p, size_t ob,
                                                           size_t nbytes) {
     uint32_t w = 0;
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < NB; ++b)
         if (ob + b < nbytes)
             w |= (uint32_t)p[ob + b] << (8 * b);
     return w;
@@ -56,15 +77,16 @@ __device__ __forceinline__ uint32_t load_code_word_masked(const uint8_t* p, size
 template <int B, int PMAX, bool OUT, bool RQ, bool MASK>
 __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
     const bool RQEF = RQ && p.rq_ef != nullptr;
-    using G = DrGeom<B>;
+    constexpr int V = dr_vec<RQ>();
+    using G = DrGeom<B, V>;
     const int lane = lane_id();
     const size_t base = tile * (size_t)G::TILE;
     const size_t n = p.n;
     const size_t nbytes = (n + 1) / 2;
 
-    uint32_t cw[PMAX][G::U];
+    uint32_t cw[PMAX][G::U];  // code words (VEC nibbles each)
     float sc[PMAX][G::U];
-    float e2[G::U][8];
+    float e2[G::U][V];
 
     // Issue every load of the tile first.
 #pragma unroll
@@ -72,34 +94,31 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
         if (q < (int)p.P) {
 #pragma unroll
             for (int u = 0; u < G::U; ++u) {
-                const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * 8;
+                const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
                 if constexpr (!MASK) {
-                    cw[q][u] = ld_stream((const uint32_t*)(p.codes[q] + i0 / 2));
+                    cw[q][u] = ld_stream((const code_word_t<V>*)(p.codes[q] + i0 / 2));
                     sc[q][u] = p.scales[q][i0 / B];
                 } else {
-                    cw[q][u] = load_code_word_masked(p.codes[q], i0 / 2, nbytes);
+                    cw[q][u] = load_code_word_masked<V / 2>(p.codes[q], i0 / 2, nbytes);
                     sc[q][u] = i0 < n ? p.scales[q][i0 / B] : 0.0f;
                 }
             }
         }
     }
-#pragma unroll
-    for (int u = 0; u < G::U; ++u)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            e2[u][j] = 0.0f;
     if (RQEF) {
 #pragma unroll
         for (int u = 0; u < G::U; ++u) {
-            const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * 8;
+            const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
             if constexpr (!MASK) {
-                f4 a = ld_stream((const f4*)(p.rq_ef + i0));
-                f4 b = ld_stream((const f4*)(p.rq_ef + i0 + 4));
-                e2[u][0] = a.x; e2[u][1] = a.y; e2[u][2] = a.z; e2[u][3] = a.w;
-                e2[u][4] = b.x; e2[u][5] = b.y; e2[u][6] = b.z; e2[u][7] = b.w;
+#pragma unroll
+                for (int h = 0; h < V / 4; ++h) {
+                    const f4 a = ld_stream((const f4*)(p.rq_ef + i0 + 4 * h));
+                    e2[u][4 * h] = a.x; e2[u][4 * h + 1] = a.y;
+                    e2[u][4 * h + 2] = a.z; e2[u][4 * h + 3] = a.w;
+                }
             } else {
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
+                for (int j = 0; j < V; ++j)
                     e2[u][j] = i0 + j < n ? p.rq_ef[i0 + j] : 0.0f;
             }
         }
@@ -108,11 +127,11 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
     // Dequantize and reduce, ascending peer order.  Peers are the outer loop
     // so the runtime test q < P is one uniform branch per peer, not a select
     // per element; alpha = 1 is skipped (multiplying by one is the identity).
-    float R[G::U][8];
+    float R[G::U][V];
 #pragma unroll
     for (int u = 0; u < G::U; ++u)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < V; ++j)
             R[u][j] = nib(cw[0][u], j) * sc[0][u];
 #pragma unroll
     for (int q = 1; q < PMAX; ++q) {
@@ -120,7 +139,7 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
 #pragma unroll
             for (int u = 0; u < G::U; ++u)
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
+                for (int j = 0; j < V; ++j)
                     R[u][j] = R[u][j] + nib(cw[q][u], j) * sc[q][u];
         }
     }
@@ -128,22 +147,23 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
 #pragma unroll
         for (int u = 0; u < G::U; ++u)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < V; ++j)
                 R[u][j] = p.alpha * R[u][j];
     }
 
     if constexpr (OUT) {
 #pragma unroll
         for (int u = 0; u < G::U; ++u) {
-            const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * 8;
+            const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
             if constexpr (!MASK) {
-                f4 a = {R[u][0], R[u][1], R[u][2], R[u][3]};
-                f4 b = {R[u][4], R[u][5], R[u][6], R[u][7]};
-                st_stream(a, (f4*)(p.out + i0));
-                st_stream(b, (f4*)(p.out + i0 + 4));
+#pragma unroll
+                for (int h = 0; h < V / 4; ++h) {
+                    const f4 a = {R[u][4 * h], R[u][4 * h + 1], R[u][4 * h + 2], R[u][4 * h + 3]};
+                    st_stream(a, (f4*)(p.out + i0 + 4 * h));
+                }
             } else {
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
+                for (int j = 0; j < V; ++j)
                     if (i0 + j < n)
                         p.out[i0 + j] = R[u][j];
             }
@@ -151,22 +171,22 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
     }
 
     if constexpr (RQ) {
-        // Without a requant EF buffer e2 is zero: R + 0 differs from R only
-        // for R = -0, which quantizes and scales exactly like +0, so one add
-        // serves both cases without a per-element select.
-        float c[G::U][8];
+        // Compensated requant input, in place (R is not needed any more).
+        float (&c)[G::U][V] = R;
+        if (RQEF) {
 #pragma unroll
-        for (int u = 0; u < G::U; ++u)
+            for (int u = 0; u < G::U; ++u)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                c[u][j] = R[u][j] + e2[u][j];
+                for (int j = 0; j < V; ++j)
+                    c[u][j] = R[u][j] + e2[u][j];
+        }
         // Beyond n the value must not enter the block max.
         if constexpr (MASK) {
 #pragma unroll
             for (int u = 0; u < G::U; ++u) {
-                const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * 8;
+                const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
+                for (int j = 0; j < V; ++j)
                     if (i0 + j >= n)
                         c[u][j] = 0.0f;
             }
@@ -177,7 +197,7 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
             for (int u = 0; u < G::U; ++u) {
                 uint32_t m = 0;
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
+                for (int j = 0; j < V; ++j)
                     m = max(m, absbits(c[u][j]));
                 bs[u] = block_scale<7>(group_max<G::LPB>(m));
             }
@@ -188,7 +208,7 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
 #pragma unroll
                 for (int u = b * G::SPB; u < (b + 1) * G::SPB; ++u)
 #pragma unroll
-                    for (int j = 0; j < 8; ++j)
+                    for (int j = 0; j < V; ++j)
                         m = max(m, absbits(c[u][j]));
                 bs[b] = block_scale<7>(group_max<kWave>(m));
             }
@@ -197,7 +217,7 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
             if (lane % G::LPB == 0) {
 #pragma unroll
                 for (int u = 0; u < G::U; ++u) {
-                    const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * 8;
+                    const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
                     if (!MASK || i0 < n)
                         p.rq_scales[i0 / B] = bs[u].s;
                 }
@@ -212,48 +232,50 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
                 }
             }
         }
-        float kf[G::U][8];
+        float kf[G::U][V];
         bool redo = false;
 #pragma unroll
         for (int u = 0; u < G::U; ++u)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < V; ++j)
                 kf[u][j] = code_fast<7>(c[u][j], bs[G::SPB == 1 ? u : u / G::SPB], redo);
         if (redo) {
 #pragma unroll
             for (int u = 0; u < G::U; ++u)
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
+                for (int j = 0; j < V; ++j)
                     kf[u][j] = code_fix<7>(c[u][j], bs[G::SPB == 1 ? u : u / G::SPB], kf[u][j]);
         }
 #pragma unroll
         for (int u = 0; u < G::U; ++u) {
             const BlockScale& s = bs[G::SPB == 1 ? u : u / G::SPB];
-            const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * 8;
+            const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
             uint32_t packed = 0;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < V; ++j) {
                 const int k = code_clamp<7>(kf[u][j]);
                 packed |= ((uint32_t)k & 0xFu) << (4 * j);
                 if (RQEF)
                     e2[u][j] = ef_update(c[u][j], k, s.s, e2[u][j], p.rq_beta_e, p.rq_beta_r);
             }
             if constexpr (!MASK) {
-                st_stream(packed, (uint32_t*)(p.rq_codes + i0 / 2));
+                st_stream((code_word_t<V>)packed, (code_word_t<V>*)(p.rq_codes + i0 / 2));
                 if (RQEF) {
-                    f4 a = {e2[u][0], e2[u][1], e2[u][2], e2[u][3]};
-                    f4 b = {e2[u][4], e2[u][5], e2[u][6], e2[u][7]};
-                    st_stream(a, (f4*)(p.rq_ef + i0));
-                    st_stream(b, (f4*)(p.rq_ef + i0 + 4));
+#pragma unroll
+                    for (int h = 0; h < V / 4; ++h) {
+                        const f4 a = {e2[u][4 * h], e2[u][4 * h + 1], e2[u][4 * h + 2],
+                                      e2[u][4 * h + 3]};
+                        st_stream(a, (f4*)(p.rq_ef + i0 + 4 * h));
+                    }
                 }
             } else {
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
+                for (int b = 0; b < V / 2; ++b)
                     if (i0 + 2 * b < n)
                         p.rq_codes[i0 / 2 + b] = (uint8_t)(packed >> (8 * b));
                 if (RQEF) {
 #pragma unroll
-                    for (int j = 0; j < 8; ++j)
+                    for (int j = 0; j < V; ++j)
                         if (i0 + j < n)
                             p.rq_ef[i0 + j] = e2[u][j];
                 }
@@ -267,7 +289,7 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
 // tiles only; the ragged last tile is a second one-wave launch (MASK).
 template <int B, int PMAX, bool OUT, bool RQ, bool MASK>
 __global__ __launch_bounds__(kBlockThreads) void dr_kernel(DrParams p) {
-    using G = DrGeom<B>;
+    using G = DrGeom<B, dr_vec<RQ>()>;
     if constexpr (MASK) {
         dr_tile<B, PMAX, OUT, RQ, true>(p, p.n / G::TILE);
     } else {
@@ -279,7 +301,7 @@ __global__ __launch_bounds__(kBlockThreads) void dr_kernel(DrParams p) {
 
 template <int B, int PMAX, bool OUT, bool RQ>
 hipError_t launch_b(const DrParams& p, hipStream_t stream) {
-    using G = DrGeom<B>;
+    using G = DrGeom<B, dr_vec<RQ>()>;
     const size_t nfull = p.n / G::TILE;
     DrParams arg = p;
     void* args[] = {(void*)&arg};
