@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-rows", action="store_true", help="skip the per-row extra workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--main-only", action="store_true",
+                    help="only the step's three kernels (no variant or extra rows): for profiling")
     ap.add_argument("--cpu-sample-elems", type=int, default=3 << 30,
                     help="gradient elements the CPU oracle processes (a multiple of 4096)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -201,35 +203,15 @@ def main():
                 "kernel": "efq_kernel<fp32, ef, B=128>", "bytes_per_launch": bytes_efq,
                 "avg_launch_ms": round(k_ms["efq"], 4)}
 
-    # LoCo variant: an EF buffer at the intra-node requant as well
-    rq_ef = torch.zeros(n1, dtype=torch.float32, device=dev)
-    ms_rqef = timed(torch, lambda: zq.zq_dequant_reduce(chunks_c, chunks_s, n1, B, 1.0,
-                                                        rq_codes=rq_codes, rq_scales=rq_scales,
-                                                        rq_ef=rq_ef, rq_beta_e=beta,
-                                                        rq_beta_r=1.0), 10)
-    del rq_ef
-    # ZeRO++ hierarchical order (4 nodes x 8 GPUs): EF quantize into permuted partitions
-    slots = zq.zeropp_slots(P1, P2)
-    ms_perm = timed(torch, lambda: zq.zq_quantize_ef_int4_permuted(g, ef, B, beta, 1.0, codes,
-                                                                   scales, slots), 10)
-    # DeepSpeed-style per-parameter quantize: the 327 tensors, one batched call
-    segs, off = [], 0
-    for t in tensors:
-        segs.append((g[off:off + t.numel], ef[off:off + t.numel],
-                     codes[off // 2:(off + t.numel) // 2], scales[off // B:(off + t.numel) // B]))
-        off += t.numel
-    table = zq.EfqSegmentTable(segs, B)
-    ms_batched = timed(torch, lambda: zq.zq_quantize_ef_int4_batched(table, B, beta, 1.0), 10)
-    del segs, table
-    rows = {
-        "efq_batched_327_tensors_fp32_b128_7.5B": row(bytes_efq, ms_batched, M),
-        "efq_permuted_zeropp_4x8_fp32_b128_7.5B": row(bytes_efq, ms_perm, M),
-        "dequant_reduce_requant_ef_p8_b128_7.5B": row(
-            dr_bytes(n1, B, P1, out=False, rq=True, rq_ef=True), ms_rqef, n1),
+    rows = {}
+    if not args.main_only:
+        rows.update(variant_rows(torch, zq, g, ef, codes, scales, chunks_c, chunks_s, rq_codes,
+                                 rq_scales, tensors, M, n1, B, P1, P2, beta, bytes_efq, dev))
+    rows.update({
         "efq_fp32_b128_7.5B": row(bytes_efq, k_ms["efq"], M),
         "dequant_reduce_requant_p8_b128_7.5B": row(bytes_dr_rq, k_ms["dr_rq"], n1),
         "dequant_reduce_p4_b128_7.5B": row(bytes_dr, k_ms["dr"], n2),
-    }
+    })
 
     # ---------------------------------------------------- CPU baseline --
     cpu = None
@@ -243,9 +225,10 @@ def main():
     del g, ef, codes, scales, rq_codes, rq_scales, out2, chunks_c, chunks_s, sub_c, sub_s
     torch.cuda.empty_cache()
 
-    if not args.no_rows:
+    extras = not (args.no_rows or args.main_only)
+    if extras:
         rows.update(extra_rows(torch, zq, synth, dev, log))
-    ceil = ceilings(torch, dev) if not args.no_rows else None
+    ceil = ceilings(torch, dev) if extras else None
     if ceil:
         roofline["ceilings_measured"] = ceil
         roofline["frac_of_mixed_ceiling"] = round(efq_gbs / ceil["torch_add_2r1w"], 4)
@@ -296,6 +279,38 @@ def ceilings(torch, dev):
     del a, b, c
     torch.cuda.empty_cache()
     return {k: round(v, 1) for k, v in out.items()}
+
+
+def variant_rows(torch, zq, g, ef, codes, scales, chunks_c, chunks_s, rq_codes, rq_scales,
+                 tensors, M, n1, B, P1, P2, beta, bytes_efq, dev):
+    """The LoCo, ZeRO++-order and per-tensor variants of the step's kernels,
+    timed on the same 7.5B buffers."""
+    # LoCo variant: an EF buffer at the intra-node requant as well
+    rq_ef = torch.zeros(n1, dtype=torch.float32, device=dev)
+    ms_rqef = timed(torch, lambda: zq.zq_dequant_reduce(chunks_c, chunks_s, n1, B, 1.0,
+                                                        rq_codes=rq_codes, rq_scales=rq_scales,
+                                                        rq_ef=rq_ef, rq_beta_e=beta,
+                                                        rq_beta_r=1.0), 10)
+    del rq_ef
+    # ZeRO++ hierarchical order (4 nodes x 8 GPUs): EF quantize into permuted partitions
+    slots = zq.zeropp_slots(P1, P2)
+    ms_perm = timed(torch, lambda: zq.zq_quantize_ef_int4_permuted(g, ef, B, beta, 1.0, codes,
+                                                                   scales, slots), 10)
+    # DeepSpeed-style per-parameter quantize: the 327 tensors, one batched call
+    segs, off = [], 0
+    for t in tensors:
+        segs.append((g[off:off + t.numel], ef[off:off + t.numel],
+                     codes[off // 2:(off + t.numel) // 2], scales[off // B:(off + t.numel) // B]))
+        off += t.numel
+    table = zq.EfqSegmentTable(segs, B)
+    ms_batched = timed(torch, lambda: zq.zq_quantize_ef_int4_batched(table, B, beta, 1.0), 10)
+    del segs, table
+    return {
+        "efq_batched_327_tensors_fp32_b128_7.5B": row(bytes_efq, ms_batched, M),
+        "efq_permuted_zeropp_4x8_fp32_b128_7.5B": row(bytes_efq, ms_perm, M),
+        "dequant_reduce_requant_ef_p8_b128_7.5B": row(
+            dr_bytes(n1, B, P1, out=False, rq=True, rq_ef=True), ms_rqef, n1),
+    }
 
 
 def row(nbytes, ms, elems):

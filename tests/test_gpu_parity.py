@@ -486,3 +486,29 @@ def test_efq_batched_matches_oracle(block, gdt, with_ef):
         assert_bits_equal(s.host(), s_o, what + " scales")
         if with_ef:
             assert_bits_equal(to_host(e), ef_o, what + " ef")
+
+
+def test_int8_random_ties_band():
+    """int8 twin of the int4 tie-band test: values on and a few ulps around
+    the rounding boundaries (k + 1/2) s of their 2048-element block."""
+    rng = np.random.default_rng(31)
+    block, nb = 2048, 64
+    out = []
+    for b in range(nb):
+        s = np.float32(2.0 ** rng.integers(-30, 30) * rng.uniform(1, 2))
+        ks = rng.integers(-127, 127, size=block) + 0.5
+        x = (ks * s).astype(np.float32)
+        for _ in range(int(rng.integers(1, 3))):
+            d = rng.integers(-1, 2, size=block)
+            target = np.where(d < 0, -np.inf, np.where(d > 0, np.inf, x)).astype(np.float32)
+            x = np.nextafter(x, target)
+        x[0] = np.float32(127) * s
+        out.append(x.astype(np.float32))
+    w = np.concatenate(out)
+    c_o, s_o = O.quant_int8(w, block)
+    codes = Guarded(w.size, torch.int8)
+    scales = Guarded(nb, torch.float32)
+    Z().zq_quant_int8(to_gpu(w), block, codes.t, scales.t)
+    torch.cuda.synchronize()
+    assert_bits_equal(codes.host().view(np.uint8), c_o.view(np.uint8), "int8 tie band codes")
+    assert_bits_equal(scales.host(), s_o, "int8 tie band scales")
