@@ -305,7 +305,9 @@ hipError_t launch_b(const DrParams& p, hipStream_t stream) {
     const size_t nfull = p.n / G::TILE;
     DrParams arg = p;
     void* args[] = {(void*)&arg};
-    constexpr Geometry geom = RQ ? kGeomReduceRequant : kGeomReduce;
+    // Requant without EF keeps a persistent grid; with EF (two more fp32
+    // streams) one tile per wave keeps more bytes in flight and is faster.
+    const Geometry geom = (RQ && p.rq_ef == nullptr) ? kGeomReduceRequant : kGeomReduce;
     hipError_t e = hipSuccess;
     if (nfull)
         e = hipLaunchKernel((const void*)&dr_kernel<B, PMAX, OUT, RQ, false>,
