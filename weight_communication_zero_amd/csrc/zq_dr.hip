@@ -62,6 +62,51 @@ __device__ __forceinline__ float nib(uint32_t w, int j) {
     return (float)((int32_t)(w << (28 - 4 * j)) >> 28);
 }
 
+// Same rounding as code_fast, by the addition of 1.5 * 2^23: for |y| < 2^22
+// the sum lies in [2^23, 2^24), where the fp32 spacing is 1, so it rounds y
+// half-to-even onto the integers (1.5 * 2^23 is even) and the subtraction
+// recovers rne(y) exactly -- as +0 where rintf gives -0, which the integer
+// code does not see.  The caller guarantees a finite block scale, so
+// |y| <= qmax (1 + 2^-22) unless `redo` is set anyway.
+template <int QMAX>
+__device__ __forceinline__ float code_fast_rne(float x, const BlockScale& b, bool& redo) {
+    const float y = x * b.inv;
+    const float k = (y + 0x1.8p23f) - 0x1.8p23f;
+    redo |= __builtin_fabsf(y - k) > tie_band<QMAX>();
+    return k;
+}
+
+// Two's-complement nibbles of V (4 or 8) integer-valued floats in [-7, 7],
+// element j in bits 4j..4j+3.  Per group of four the biased digits k_j + 8
+// lie in [1, 15], so W = sum (k_j + 8) 16^j has no carries between digits;
+// it is an integer below 2^16, exact in fp32, and adding 1.5 * 2^23 puts it
+// in the low mantissa bits (the bias 0x8888 rides on that constant).
+// Flipping bit 3 of every digit (xor 0x8...8) then gives k_j mod 16.  The
+// two groups of eight are joined by a byte permute.
+template <int V>
+__device__ __forceinline__ uint32_t pack_nibbles_f(const float (&k)[V]) {
+    uint32_t h[2];
+#pragma unroll
+    for (int g = 0; g < V / 4; ++g) {
+        const float lo = __builtin_fmaf(k[4 * g + 1], 16.0f, k[4 * g]);
+        const float hi = __builtin_fmaf(k[4 * g + 3], 16.0f, k[4 * g + 2]);
+        h[g] = fbits(__builtin_fmaf(hi, 256.0f, lo) + (0x1.8p23f + (float)0x8888));
+    }
+    if constexpr (V == 8)
+        return __builtin_amdgcn_perm(h[1], h[0], 0x05040100u) ^ 0x88888888u;
+    else
+        return (h[0] ^ 0x8888u) & 0xFFFFu;
+}
+
+// ef_update with the code given as an exact integer-valued float (+0 for 0).
+__device__ __forceinline__ float ef_update_f(float c, float k, float s, float e, float be, float br) {
+    float d = k * s;
+    float r = c - d;
+    float t1 = be * e;
+    float t2 = br * r;
+    return t1 + t2;
+}
+
 // Up to NB code bytes starting at byte offset ob, only those below nbytes.
 template <int NB>
 __device__ __forceinline__ uint32_t load_code_word_masked(const uint8_t* p, size_t ob,
@@ -232,34 +277,53 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
                 }
             }
         }
+        // Fast codes: rne(c * rcp(s)) by the 1.5 * 2^23 addition.  A tile
+        // falls back to the IEEE quotient when an element is in the tie band
+        // or a block scale is subnormal, infinite or NaN (uniform branch).
         float kf[G::U][V];
         bool redo = false;
 #pragma unroll
-        for (int u = 0; u < G::U; ++u)
+        for (int u = 0; u < G::U; ++u) {
+            const BlockScale& b = bs[G::SPB == 1 ? u : u / G::SPB];
+            redo |= b.exact | !(b.s <= 0x1.fffffep127f);
 #pragma unroll
             for (int j = 0; j < V; ++j)
-                kf[u][j] = code_fast<7>(c[u][j], bs[G::SPB == 1 ? u : u / G::SPB], redo);
-        if (redo) {
+                kf[u][j] = code_fast_rne<7>(c[u][j], b, redo);
+        }
+        uint32_t packed[G::U];
+        if (__builtin_amdgcn_ballot_w64(redo) == 0) {
+            // Every |code| <= 7 here: pack the float codes, and use them as
+            // exact integers in the error feedback.
 #pragma unroll
-            for (int u = 0; u < G::U; ++u)
+            for (int u = 0; u < G::U; ++u) {
+                packed[u] = pack_nibbles_f<V>(kf[u]);
+                if (RQEF) {
+                    const BlockScale& b = bs[G::SPB == 1 ? u : u / G::SPB];
 #pragma unroll
-                for (int j = 0; j < V; ++j)
-                    kf[u][j] = code_fix<7>(c[u][j], bs[G::SPB == 1 ? u : u / G::SPB], kf[u][j]);
+                    for (int j = 0; j < V; ++j)
+                        e2[u][j] = ef_update_f(c[u][j], kf[u][j], b.s, e2[u][j], p.rq_beta_e,
+                                               p.rq_beta_r);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < G::U; ++u) {
+                const BlockScale& b = bs[G::SPB == 1 ? u : u / G::SPB];
+                packed[u] = 0;
+#pragma unroll
+                for (int j = 0; j < V; ++j) {
+                    const int k = code_clamp<7>(code_fix<7>(c[u][j], b, kf[u][j]));
+                    packed[u] |= ((uint32_t)k & 0xFu) << (4 * j);
+                    if (RQEF)
+                        e2[u][j] = ef_update(c[u][j], k, b.s, e2[u][j], p.rq_beta_e, p.rq_beta_r);
+                }
+            }
         }
 #pragma unroll
         for (int u = 0; u < G::U; ++u) {
-            const BlockScale& s = bs[G::SPB == 1 ? u : u / G::SPB];
             const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
-            uint32_t packed = 0;
-#pragma unroll
-            for (int j = 0; j < V; ++j) {
-                const int k = code_clamp<7>(kf[u][j]);
-                packed |= ((uint32_t)k & 0xFu) << (4 * j);
-                if (RQEF)
-                    e2[u][j] = ef_update(c[u][j], k, s.s, e2[u][j], p.rq_beta_e, p.rq_beta_r);
-            }
             if constexpr (!MASK) {
-                st_stream((code_word_t<V>)packed, (code_word_t<V>*)(p.rq_codes + i0 / 2));
+                st_stream((code_word_t<V>)packed[u], (code_word_t<V>*)(p.rq_codes + i0 / 2));
                 if (RQEF) {
 #pragma unroll
                     for (int h = 0; h < V / 4; ++h) {
@@ -272,7 +336,7 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
 #pragma unroll
                 for (int b = 0; b < V / 2; ++b)
                     if (i0 + 2 * b < n)
-                        p.rq_codes[i0 / 2 + b] = (uint8_t)(packed >> (8 * b));
+                        p.rq_codes[i0 / 2 + b] = (uint8_t)(packed[u] >> (8 * b));
                 if (RQEF) {
 #pragma unroll
                     for (int j = 0; j < V; ++j)
