@@ -185,6 +185,9 @@ def main():
     torch.cuda.synchronize()
     step_ms = t_start.elapsed_time(t_end) / max(args.steps, 1)
     k_ms = {k: float(np.mean(timer.ms(k))) for k in ("efq", "dr_rq", "dr")}
+    # spread of the per-launch event times over the timed steps
+    k_pct = {k: [round(float(v), 4) for v in np.percentile(timer.ms(k), [10, 50, 90])]
+             for k in ("efq", "dr_rq", "dr")}
     value = bytes_step / (step_ms * 1e-3) / 1e9
     log(f"step {step_ms:.3f} ms, {value:.1f} GB/s; kernels (ms) {k_ms}")
 
@@ -212,6 +215,9 @@ def main():
         "dequant_reduce_requant_p8_b128_7.5B": row(bytes_dr_rq, k_ms["dr_rq"], n1),
         "dequant_reduce_p4_b128_7.5B": row(bytes_dr, k_ms["dr"], n2),
     })
+    for name, k in (("efq_fp32_b128_7.5B", "efq"), ("dequant_reduce_requant_p8_b128_7.5B", "dr_rq"),
+                    ("dequant_reduce_p4_b128_7.5B", "dr")):
+        rows[name]["ms_p10_p50_p90"] = k_pct[k]
 
     # ---------------------------------------------------- CPU baseline --
     cpu = None
