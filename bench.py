@@ -504,9 +504,31 @@ def timed(torch, fn, reps, warm=2):
     return float(np.median([a.elapsed_time(b) for a, b in evs]))
 
 
+def timed_cold(torch, fn, reps, flush):
+    """Median ms of `fn` when each call follows a write of `flush` (>= 1 GiB),
+    which evicts the 4 MB L2s and the 256 MB MALL: the HBM-cold time."""
+    evs = []
+    for _ in range(reps):
+        flush.fill_(1.0)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    import numpy as np
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+
+def cold_fields(nbytes, ms):
+    return {"cold_ms": round(ms, 4), "cold_GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def extra_rows(torch, zq, synth, dev, log):
     """The other rows of the path, each on its own workload."""
     rows = {}
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
     # qwZ: bf16 weights of the ~0.85B model, block 2048
     t3 = synth.llama_0p85b()
     n = synth.total(t3)
@@ -554,8 +576,10 @@ def extra_rows(torch, zq, synth, dev, log):
     st = torch.cuda.current_stream().cuda_stream
     dp, sp = dsh.data_ptr(), ssh.data_ptr()
     ms = timed_burst(torch, lambda: zq.lib.zq_sr_accumulate(dp, sp, shard, 0, off, 0, st), 200)
-    rows["sr_accumulate_bf16_gpt2_rank3_shard"] = dict(row(6 * shard, ms, shard),
-                                                       note="cache-resident (93 MB)")
+    ms_c = timed_cold(torch, lambda: zq.lib.zq_sr_accumulate(dp, sp, shard, 0, off, 0, st), 20, flush)
+    rows["sr_accumulate_bf16_gpt2_rank3_shard"] = dict(
+        row(6 * shard, ms, shard), **cold_fields(6 * shard, ms_c),
+        note="93 MB: back-to-back calls run cache-resident; cold_* follow a 1 GiB write")
     log("SR rows", rows["sr_accumulate_bf16_gpt2_124M_full"])
     del dst, src, dsh, ssh
 
@@ -574,6 +598,7 @@ def extra_rows(torch, zq, synth, dev, log):
     nbytes = sum(6 * m + 2 * src.numel() for _, src, m, _, _, _ in segs)
     table = zq.SrSegmentTable(segs)
     ms_b = timed_burst(torch, lambda: zq.zq_sr_accumulate_batched(table, zero_src=True), 50)
+    ms_bc = timed_cold(torch, lambda: zq.zq_sr_accumulate_batched(table, zero_src=True), 20, flush)
 
     def loop():
         for d_, s_, m_, o_, sd_, cb_ in segs:
@@ -581,7 +606,7 @@ def extra_rows(torch, zq, synth, dev, log):
             s_.zero_()
     ms_l = timed_burst(torch, loop, 5)
     rows["sr_accumulate_batched_gpt2_148_tensors_rank3"] = dict(
-        row(nbytes, ms_b, n // 8),
+        row(nbytes, ms_b, n // 8), **cold_fields(nbytes, ms_bc),
         note=f"one call for 148 tensors incl. clearing the reduced buffers (marshalled table, "
              f"back-to-back calls); the same work as a Python loop of 148 single calls + 148 "
              f"torch zero_() takes {ms_l:.3f} ms, host overhead included",
@@ -600,8 +625,13 @@ def extra_rows(torch, zq, synth, dev, log):
     a4 = (g4.data_ptr(), e4.data_ptr(), c4.data_ptr(), s4.data_ptr())
     ms = timed_burst(torch, lambda: zq.lib.zq_quantize_ef_int4(a4[0], 1, a4[1], n, 256, 1.0, 1.0,
                                                                a4[2], a4[3], st), 200)
-    rows["efq_bf16_b256_4x2^20"] = dict(row(efq_bytes(n, 256, 2), ms, n),
-                                       note="cache-resident (44 MB)")
+    ms_c = timed_cold(torch, lambda: zq.lib.zq_quantize_ef_int4(a4[0], 1, a4[1], n, 256, 1.0, 1.0,
+                                                                 a4[2], a4[3], st), 20, flush)
+    rows["efq_bf16_b256_4x2^20"] = dict(
+        row(efq_bytes(n, 256, 2), ms, n), **cold_fields(efq_bytes(n, 256, 2), ms_c),
+        note="44 MB: back-to-back calls run cache-resident and launch-bound; cold_* follow a "
+             "1 GiB write")
+    del flush
     torch.cuda.empty_cache()
     return rows
 
