@@ -223,6 +223,31 @@ __device__ __forceinline__ size_t wave_id() {
     return (size_t)blockIdx.x * (blockDim.x >> 6) + w;
 }
 __device__ __forceinline__ size_t wave_count() { return (size_t)gridDim.x * (blockDim.x >> 6); }
+
+// The same wave index with the workgroups taken in an XCD-aware order, for a
+// grid of THREADS-thread workgroups that each own THREADS / 64 tiles.  The
+// dispatcher hands workgroup b to XCD b % 8 (MI355X has 8 XCDs, each with its
+// own L2).  Within every block of 8 C consecutive workgroups, XCD x takes the
+// C workgroups starting at x C, so each XCD streams one contiguous run of
+// ZQ_XCD_CHUNK tiles at a time instead of every eighth workgroup; a trailing
+// partial block keeps the dispatch order.  The map permutes the workgroup
+// indices, so each tile is still visited exactly once.  ZQ_XCD_CHUNK = 0
+// turns it off.
+#ifndef ZQ_XCD_CHUNK
+#define ZQ_XCD_CHUNK 16384
+#endif
+template <uint32_t THREADS>
+__device__ __forceinline__ size_t stream_wave_id() {
+    constexpr size_t WPG = THREADS / kWave;
+    constexpr size_t C = ZQ_XCD_CHUNK / WPG;
+    size_t b = blockIdx.x;
+    if constexpr (C > 0) {
+        const size_t full = (size_t)gridDim.x / (8 * C) * (8 * C);
+        if (b < full)
+            b = b / (8 * C) * (8 * C) + (b % 8) * C + (b / 8) % C;
+    }
+    return b * WPG + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
 }  // namespace zq

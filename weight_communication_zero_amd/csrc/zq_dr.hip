@@ -358,6 +358,8 @@ __global__ __launch_bounds__(kBlockThreads) void dr_kernel(DrParams p) {
         dr_tile<B, PMAX, OUT, RQ, true>(p, p.n / G::TILE);
     } else {
         const size_t nfull = p.n / G::TILE;
+        // Plain dispatch order: the XCD-contiguous order of the streaming
+        // kernels measured slower here (P peer streams per XCD run).
         for (size_t t = wave_id(); t < nfull; t += wave_count())
             dr_tile<B, PMAX, OUT, RQ, false>(p, t);
     }

@@ -219,7 +219,7 @@ __global__ __launch_bounds__(kBlockThreads) void efq_kernel(const void* __restri
         efq_tile<BF16, EF, B, true>(g, ef, n, beta_e, beta_r, codes, scales, n / G::TILE);
     } else {
         const size_t nfull = n / G::TILE;
-        for (size_t t = wave_id(); t < nfull; t += wave_count())
+        for (size_t t = stream_wave_id<kGeomStream.threads>(); t < nfull; t += wave_count())
             efq_tile<BF16, EF, B, false>(g, ef, n, beta_e, beta_r, codes, scales, t);
     }
 }
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(kBlockThreads) void efq_perm_kernel(const void* __r
                                     perm_map(perm, t * G::TILE));
     } else {
         const size_t nfull = n / G::TILE;
-        for (size_t t = wave_id(); t < nfull; t += wave_count())
+        for (size_t t = stream_wave_id<kGeomStream.threads>(); t < nfull; t += wave_count())
             efq_tile<BF16, EF, B, false>(g, ef, n, beta_e, beta_r, codes, scales, t,
                                          perm_map(perm, t * G::TILE));
     }
@@ -326,7 +326,7 @@ __device__ __forceinline__ uint32_t find_segment(const EfqBatch& b, uint32_t t) 
 template <bool BF16, bool EF, int B, bool MASK>
 __global__ __launch_bounds__(kBlockThreads) void efq_batched_kernel(EfqBatch b) {
     using G = EfqGeom<B>;
-    for (size_t ts = wave_id(); ts < b.total; ts += wave_count()) {
+    for (size_t ts = stream_wave_id<kGeomStream.threads>(); ts < b.total; ts += wave_count()) {
         const uint32_t t = (uint32_t)ts;
         const uint32_t s = find_segment(b, t);
         const EfqSegment& g = b.seg[s];

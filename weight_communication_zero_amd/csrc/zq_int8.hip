@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kBlockThreads) void q8_kernel(const void* __restric
         q8_tile<BF16, B, true>(w, n, codes, scales, n / G::TILE);
     } else {
         const size_t nfull = n / G::TILE;
-        for (size_t t = wave_id(); t < nfull; t += wave_count())
+        for (size_t t = stream_wave_id<kGeomStream.threads>(); t < nfull; t += wave_count())
             q8_tile<BF16, B, false>(w, n, codes, scales, t);
     }
 }
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(kBlockThreads) void dq8_kernel(const int8_t* __rest
         dq8_tile<BF16OUT, true>(codes, scales, n, log2b, out, n / kDqTile);
     } else {
         const size_t nfull = n / kDqTile;
-        for (size_t t = wave_id(); t < nfull; t += wave_count())
+        for (size_t t = stream_wave_id<kGeomStream.threads>(); t < nfull; t += wave_count())
             dq8_tile<BF16OUT, false>(codes, scales, n, log2b, out, t);
     }
 }

@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kBlockThreads) void sr_kernel(uint16_t* __restrict_
         sr_tile<PHASE, ZERO, true>(dst, src, n, k0, k1, cbase8, n / kSrTile);
     } else {
         const size_t nfull = n / kSrTile;
-        for (size_t t = wave_id(); t < nfull; t += wave_count())
+        for (size_t t = stream_wave_id<kGeomStream.threads>(); t < nfull; t += wave_count())
             sr_tile<PHASE, ZERO, false>(dst, src, n, k0, k1, cbase8, t);
     }
 }
@@ -228,7 +228,7 @@ __device__ __forceinline__ void zero_seg_tile(const SrSegment& g, uint64_t local
 }
 
 __global__ __launch_bounds__(kBlockThreads) void sr_batched_kernel(SrBatch b) {
-    for (size_t ts = wave_id(); ts < b.total; ts += wave_count()) {
+    for (size_t ts = stream_wave_id<kGeomStream.threads>(); ts < b.total; ts += wave_count()) {
         const uint32_t t = (uint32_t)ts;
         // Segment of tile t: the number of cumulative counts it has passed.
         // Independent compares against table entries the compiler loads once,
