@@ -18,7 +18,7 @@
 #include "zq_launch.h"
 
 #ifndef ZQ_EFQ_U
-#define ZQ_EFQ_U 4  // sub-vectors of 256 elements per wave tile
+#define ZQ_EFQ_U 2  // sub-vectors of 256 elements per wave tile
 #endif
 
 namespace zq {
@@ -347,9 +347,16 @@ hipError_t launch_batched_b(const EfqSegment* segs, uint32_t n_seg, float be, fl
             bt.beta_e = be;
             bt.beta_r = br;
             uint64_t tiles = 0;
+            // A launch takes segments while its tile count (32-bit in the
+            // kernel's table) stays below 2^32; one segment (at most 2^40
+            // elements) has fewer than 2^32 tiles.
+            static_assert(G::TILE >= 512, "2^40-element segments need tiles of >= 512");
             while (i < n_seg && bt.nseg < (uint32_t)kEfqSegs) {
-                const EfqSegment& g = segs[i++];
+                const EfqSegment& g = segs[i];
                 const uint64_t t = pass == 0 ? g.n / G::TILE : (g.n % G::TILE ? 1 : 0);
+                if (tiles + t > UINT32_MAX)
+                    break;  // the next launch starts with this segment
+                ++i;
                 if (t == 0)
                     continue;
                 bt.seg[bt.nseg] = g;

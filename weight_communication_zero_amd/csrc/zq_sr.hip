@@ -266,8 +266,9 @@ hipError_t launch_sr_accumulate(uint16_t* dst, uint16_t* src, size_t n, uint64_t
 
 hipError_t launch_sr_accumulate_batched(const SrSegment* segs, uint32_t n_seg, bool zero_src,
                                         hipStream_t stream) {
-    // Segments are at most 2^40 elements (checked by the ABI layer), so a
-    // launch of up to 32 of them has fewer than 2^32 tiles.
+    // Segments are at most 2^40 elements (checked by the ABI layer), so one
+    // has at most 2^31 tiles; a launch takes segments while its tile count
+    // (32-bit in the kernel's table) stays below 2^32.
     uint32_t i = 0;
     while (i < n_seg) {
         SrBatch b = {};
@@ -275,9 +276,12 @@ hipError_t launch_sr_accumulate_batched(const SrSegment* segs, uint32_t n_seg, b
         uint32_t nseg = 0;
         uint64_t tiles = 0;
         while (i < n_seg && nseg < (uint32_t)kSegsPerLaunch) {
-            const SrSegment& g = segs[i++];
+            const SrSegment& g = segs[i];
             const uint64_t sr = (g.n + kSrTile - 1) / kSrTile;
             const uint64_t zt = zero_src ? (g.len - g.n + kSrTile - 1) / kSrTile : 0;
+            if (tiles + sr + zt > UINT32_MAX)
+                break;  // the next launch starts with this segment
+            ++i;
             if (sr + zt == 0)
                 continue;
             b.seg[nseg] = g;
