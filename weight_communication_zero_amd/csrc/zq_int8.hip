@@ -159,7 +159,10 @@ __global__ __launch_bounds__(kBlockThreads) void q8_kernel(const void* __restric
 
 // Dequantize: lane l of sub-vector u owns 8 codes (one 8-byte load) that lie
 // in a single block (B >= 32), so each lane needs one scale and no exchange.
-constexpr int kDqU = 4;
+#ifndef ZQ_DQ_U
+#define ZQ_DQ_U 2
+#endif
+constexpr int kDqU = ZQ_DQ_U;
 constexpr int kDqSub = kWave * 8;
 constexpr int kDqTile = kDqSub * kDqU;
 

@@ -17,7 +17,10 @@
 namespace zq {
 namespace {
 
-constexpr int kSrU = 2;
+#ifndef ZQ_SR_U
+#define ZQ_SR_U 2
+#endif
+constexpr int kSrU = ZQ_SR_U;
 constexpr int kSrSub = kWave * 8;
 constexpr int kSrTile = kSrSub * kSrU;
 
