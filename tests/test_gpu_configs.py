@@ -134,9 +134,16 @@ def test_int8_weights_0p85b_sampled_blocks():
     codes = torch.empty(n, dtype=torch.int8, device="cuda")
     scales = torch.empty(n // B, dtype=torch.float32, device="cuda")
     wd = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    # poison: -128 is never a code (clamp to +-127), NaN never a finite block's scale
+    codes.fill_(-128)
+    scales.fill_(float("nan"))
+    wd.fill_(float("nan"))
     Z().zq_quant_int8(w, B, codes, scales)
     Z().zq_dequant_int8(codes, scales, B, wd)
     torch.cuda.synchronize()
+    assert not bool((codes == -128).any()), "int8 codes left unwritten"
+    assert not bool(torch.isnan(scales).any()), "int8 scales left unwritten"
+    assert not bool(torch.isnan(wd).any()), "dequantized weights left unwritten"
     nb = n // B
     rng = np.random.default_rng(3)
     blocks = np.unique(np.concatenate([[0, nb - 1], rng.integers(0, nb, size=254)]))
@@ -202,6 +209,15 @@ def run_two_level(tensors, tag, steps, levels, n_sample, seed, beta=(0.9, 1.0), 
                 rq_ef_o[:] = 0.0
         synth.fill_model(g, tensors, std=1e-3, seed=synth.seed_for(tag, "grad", step=step),
                          heavy_tails=True)
+        # Poison every output with values the kernels never produce for
+        # finite inputs (nibble 8 = -8, NaN), so the whole-buffer checks below
+        # see any tile a launch geometry failed to visit.
+        codes.fill_(0x88)
+        scales.fill_(float("nan"))
+        out.fill_(float("nan"))
+        if two:
+            rqc.fill_(0x88)
+            rqs.fill_(float("nan"))
         Z().zq_quantize_ef_int4(g, ef, B, beta[0], beta[1], codes, scales)
         if two:
             Z().zq_dequant_reduce(chunks_c, chunks_s, n1, B, alpha1, rq_codes=rqc, rq_scales=rqs,
@@ -210,11 +226,17 @@ def run_two_level(tensors, tag, steps, levels, n_sample, seed, beta=(0.9, 1.0), 
         else:
             Z().zq_dequant_reduce(chunks_c, chunks_s, n1, B, alpha1, out=out)
         torch.cuda.synchronize()
+        what = f"{tag} step {step}"
+        for name, c in (("codes", codes),) + ((("requant codes", rqc),) if two else ()):
+            assert not bool(((c & 0x0F) == 8).any() | ((c >> 4) == 8).any()), \
+                what + f": {name} left unwritten (nibble -8 present)"
+        for name, t in (("scales", scales), ("reduced sum", out)) + \
+                ((("requant scales", rqs),) if two else ()):
+            assert not bool(torch.isnan(t).any()), what + f": {name} left unwritten (NaN present)"
 
         # oracle: EF quantize of the tracked blocks
         g_h = gather_blocks(g, L0, B)
         c0, s0 = O.quantize_ef_int4(g_h, ef_o, B, beta[0], beta[1])
-        what = f"{tag} step {step}"
         assert_bits_equal(int4_block_bytes(codes, L0, B), c0, what + " codes")
         assert_bits_equal(to_host(scales)[L0], s0, what + " scales")
         assert_bits_equal(gather_blocks(ef, L0, B), ef_o, what + " ef")
