@@ -391,7 +391,30 @@ def cpu_baseline(g_host, B, beta, P1, P2):
             "seconds": round(t3 - t0, 2),
             "split_s": {"efq": round(t1 - t0, 2), "dr_rq": round(t2 - t1, 2),
                         "dr": round(t3 - t2, 2)},
-            "host": platform.processor() or platform.machine(), "host_nproc": os.cpu_count()}
+            "host": host_cpu_model() or platform.processor() or platform.machine(),
+            "host_nproc": os.cpu_count(), "host_mem_gib": host_mem_gib()}
+
+
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def host_mem_gib():
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal:"):
+                    return round(int(line.split()[1]) / (1 << 20), 1)
+    except OSError:
+        pass
+    return None
 
 
 def summarize_rocprof(d):
