@@ -259,6 +259,7 @@ def main():
             "elements": M, "block": B, "peers_intra": P1, "peers_inter": P2,
             "bytes_per_step": bytes_step, "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
             "gpu": torch.cuda.get_device_name(0),
+            "gpu_arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
