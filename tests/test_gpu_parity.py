@@ -512,3 +512,41 @@ def test_int8_random_ties_band():
     torch.cuda.synchronize()
     assert_bits_equal(codes.host().view(np.uint8), c_o.view(np.uint8), "int8 tie band codes")
     assert_bits_equal(scales.host(), s_o, "int8 tie band scales")
+
+
+@pytest.mark.parametrize("with_rq_ef", [False, True])
+def test_requant_exact_ties(with_rq_ef):
+    """Reduced sums that sit exactly on half-integers of the requant scale:
+    peer 0 has scale 2^-10 with a code 7 in every block (so the requant scale
+    is 2^-10 again), peer 1 adds +-1 at scale 2^-11.  Ties appear only in the
+    first two 1024-element tiles, so those tiles take the IEEE path and the
+    rest the fast path; the codes must round half to even like the oracle."""
+    rng = np.random.default_rng(77)
+    n, block = 8192, 128
+    k0 = rng.integers(-6, 7, size=n)
+    k0[::block] = 7
+    k1 = np.zeros(n, dtype=np.int64)
+    k1[:2048] = rng.choice([-1, 0, 1], size=2048)
+    k1[:2048:block] = 0
+
+    def pack(k):
+        u = (k & 0xF).astype(np.uint8)
+        return (u[0::2] | (u[1::2] << 4)).astype(np.uint8)
+    codes = [pack(k0), pack(k1)]
+    scales = [np.full(n // block, 2.0 ** -10, np.float32), np.full(n // block, 2.0 ** -11, np.float32)]
+    rq_ef_h = grad_values(n, seed=5, std=1e-6) if with_rq_ef else None
+    rq_ef_o = rq_ef_h.copy() if with_rq_ef else None
+    _, rqc_o, rqs_o = O.dequant_reduce(codes, scales, n, block, 1.0, want_out=False, requant=True,
+                                       rq_ef=rq_ef_o, rq_beta_e=0.9, rq_beta_r=1.0)
+    rqc = Guarded(n // 2, torch.uint8)
+    rqs = Guarded(n // block, torch.float32)
+    rq_ef = to_gpu(rq_ef_h) if with_rq_ef else None
+    Z().zq_dequant_reduce([to_gpu(c) for c in codes], [to_gpu(s) for s in scales], n, block, 1.0,
+                          rq_codes=rqc.t, rq_scales=rqs.t, rq_ef=rq_ef, rq_beta_e=0.9,
+                          rq_beta_r=1.0)
+    torch.cuda.synchronize()
+    what = f"requant ties rq_ef={with_rq_ef}"
+    assert_bits_equal(rqc.host(), rqc_o, what + " codes")
+    assert_bits_equal(rqs.host(), rqs_o, what + " scales")
+    if with_rq_ef:
+        assert_bits_equal(to_host(rq_ef), rq_ef_o, what + " rq_ef")
