@@ -163,8 +163,8 @@ def make_chunks(P, n, block, seed, raw=False):
     return codes, scales
 
 
-def check_dr(P, n, block, alpha, want_out, requant, with_rq_ef, seed, raw=False):
-    codes, scales = make_chunks(P, n, block, seed, raw=raw)
+def check_dr(P, n, block, alpha, want_out, requant, with_rq_ef, seed, raw=False, chunks=None):
+    codes, scales = chunks if chunks is not None else make_chunks(P, n, block, seed, raw=raw)
     rq_ef_host = grad_values(n, seed=seed + 99, std=1e-6) if with_rq_ef else None
     rq_ef_o = rq_ef_host.copy() if with_rq_ef else None
     out_o, rqc_o, rqs_o = O.dequant_reduce(codes, scales, n, block, alpha, want_out=want_out,
@@ -221,6 +221,54 @@ def test_dequant_reduce_requant(block, flags):
 def test_dequant_reduce_alpha_and_raw_codes(alpha):
     check_dr(6, 4096 * 3 + 5, 128, alpha, True, True, True, seed=11, raw=True)
     check_dr(16, 2048 + 1, 64, alpha, True, True, False, seed=12, raw=True)
+
+
+def extreme_scale_chunks(P, n, block, seed, top):
+    """Raw nibbles (-8 included unless the scales reach 2^120) with positive
+    scales log-uniform from the smallest subnormal up to 2^top, and blocks
+    with the scales +0, -0, a negative value and the smallest subnormal (and
+    for top > 120 also 2^125 and the float just below it).  A zero scale
+    with a negative code gives -0, which the sums must keep."""
+    rng = np.random.default_rng(seed)
+    nb = -(-n // block)
+    per_tile = 1024 // block if block <= 1024 else 1
+    codes, scales = [], []
+    for p in range(P):
+        c = rng.integers(0, 256, size=(n + 1) // 2, dtype=np.uint8)
+        if n % 2:
+            c[-1] &= 0x0F
+        e = rng.uniform(-149, top, size=nb)
+        s = np.exp2(e).astype(np.float32)
+        specials = [np.float32(0.0), np.float32(-0.0), np.float32(-3e-5), np.float32(1e-45)]
+        if top > 120:
+            specials += [np.float32(2.0 ** 125), np.nextafter(np.float32(2.0 ** 125), np.float32(0))]
+        for t, v in enumerate(specials):
+            b = ((t + 1) * per_tile) % nb
+            if p == t % P:
+                s[b] = v
+        if top > 120:
+            # keep k * s finite: no -8 code and |k| <= 7 where s is huge
+            lo, hi = c & 0x0F, c >> 4
+            lo = np.where(lo == 8, 7, lo)
+            hi = np.where(hi == 8, 7, hi)
+            c = (lo | (hi << 4)).astype(np.uint8)
+        codes.append(c)
+        scales.append(s)
+    return codes, scales
+
+
+@pytest.mark.parametrize("block", [32, 128, 1024, 4096])
+@pytest.mark.parametrize("flags", [(True, False, False), (False, True, False), (True, True, True)])
+def test_dequant_reduce_extreme_scales(block, flags):
+    want_out, requant, rqef = flags
+    n = max(1024, block) * 9 + 3
+    # moderate scales: every peer count; huge scales (up to 2^125): one peer,
+    # so that sums stay finite
+    for P in (2, 8):
+        check_dr(P, n, block, 1.0, want_out, requant, rqef, seed=block + P,
+                 chunks=extreme_scale_chunks(P, n, block, block + P, top=30))
+    check_dr(1, n, block, 1.0, want_out, requant, rqef, seed=block,
+             chunks=extreme_scale_chunks(1, n, block, block, top=124.99))
 
 
 # ---------------------------------------------------------------- qwZ int8 --

@@ -12,6 +12,8 @@ from __future__ import annotations
 import glob
 import os
 import subprocess
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -37,15 +39,26 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, extra: list[str] | None = None, out: str | None = None) -> str:
-    out = out or LIB
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra or []), "-o", tmp, *sources()]
+def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr[-8000:]}")
+
+
+def build(verbose: bool = False, extra: list[str] | None = None, out: str | None = None) -> str:
+    """Compile every source to an object in parallel, then link the shared
+    library (each object carries its own gfx950 code object)."""
+    out = out or LIB
+    tmp = out + ".tmp"
+    with tempfile.TemporaryDirectory(prefix="zq_build_") as d:
+        objs = [os.path.join(d, os.path.basename(s) + ".o") for s in sources()]
+        jobs = [[HIPCC, *FLAGS, *(extra or []), "-c", "-o", o, s] for s, o in zip(sources(), objs)]
+        with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1, 8)) as ex:
+            for f in [ex.submit(_run, j, verbose) for j in jobs]:
+                f.result()
+        _run([HIPCC, *FLAGS, *(extra or []), "-o", tmp, *objs], verbose)
     os.replace(tmp, out)
     return out
 
