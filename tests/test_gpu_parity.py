@@ -510,11 +510,11 @@ def test_hierarchical_qgz_delivers_each_rank_its_partition():
 @pytest.mark.parametrize("gdt", ["fp32", "bf16"])
 @pytest.mark.parametrize("with_ef", [False, True])
 def test_efq_batched_matches_oracle(block, gdt, with_ef):
-    """45 tensors (two launches of at most 32 plus their tail launches),
+    """170 tensors (three launches of at most 80 plus their tail launches),
     ragged lengths from 1 element to several tiles."""
     rng = np.random.default_rng(block * 7 + (gdt == "bf16") * 3 + with_ef)
     segs_g, exp = [], []
-    for i in range(45):
+    for i in range(170):
         n = int(rng.choice([1, 3, block - 1, block, 1024, 4096, 4096 + 17, 3 * max(1024, block) + 5,
                             20000]))
         x = grad_values(n, seed=300 + i, special=True, block=block)

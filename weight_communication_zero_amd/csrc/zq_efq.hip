@@ -300,8 +300,13 @@ hipError_t launch_perm_t(const void* g, float* ef, size_t n, uint32_t block, flo
 // Batched segments.  The main launch runs the full tiles of up to kEfqSegs
 // segments; a second launch runs every segment's ragged last tile (masked),
 // one wave each.  A wave finds its segment by binary search over the
-// cumulative tile counts in the kernel arguments (five scalar loads).
-constexpr int kEfqSegs = 32;
+// cumulative tile counts in the kernel arguments (seven scalar loads).
+// 80 segments (3.5 KB of kernel arguments) take the 7.5B model's 327 tensors
+// in 5 launches instead of 11.
+#ifndef ZQ_EFQ_SEGS
+#define ZQ_EFQ_SEGS 80
+#endif
+constexpr int kEfqSegs = ZQ_EFQ_SEGS;
 
 struct EfqBatch {
     EfqSegment seg[kEfqSegs];
