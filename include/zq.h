@@ -129,7 +129,7 @@ zq_status zq_quantize_ef_int4_permuted(const void *g, zq_dtype g_dtype, float *e
  * call: DeepSpeed's LoCo path quantizes parameter by parameter, each with
  * its own error-feedback buffer ([LoCo] review thread: the EF buffer kept on
  * each parameter, p.inter_ef_buf); here one pass covers all of them, up to
- * 32 tensors per kernel launch (the table travels in the kernel arguments;
+ * 80 tensors per kernel launch (the table travels in the kernel arguments;
  * nothing is allocated).
  *
  * Segment i is exactly zq_quantize_ef_int4(seg.g, g_dtype, seg.ef, seg.n,
@@ -237,7 +237,7 @@ zq_status zq_sr_accumulate(uint16_t *dst_bf16, uint16_t *src_bf16, size_t n, uin
  * Segment i does exactly what zq_sr_accumulate(seg.dst, seg.src +
  * seg.src_offset, seg.n, seg.seed, seg.counter_base, 0) does, and then, when
  * zero_src != 0, sets ALL seg.src_len elements of seg.src to 0 (the read
- * slice after it is read).  Segments run in one pass, up to 32 per kernel
+ * slice after it is read).  Segments run in one pass, up to 50 per kernel
  * launch (the table travels in the kernel arguments; nothing is allocated).
  *
  *   segs      HOST array of n_seg segments (read during the call only).
