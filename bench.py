@@ -263,9 +263,29 @@ def main():
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "pages_context": pages_context(zq, M),
         "rows": rows,
     }
     print(json.dumps(line), flush=True)
+
+
+def pages_context(zq, M):
+    """The pages' own system-level figures, for context only: they publish
+    no kernel-level number.  ZeRO++ notes, abstract and section 1.2: ZeRO-3
+    moves 3M per step (two fp16 weight all-gathers and one fp16 gradient
+    reduce-scatter), ZeRO++ 0.75M (int8 weights, no inter-node backward
+    gather, int4 gradients), and trains 2.16x faster at 384 GPUs (GPU model
+    and workload not stated).  The bytes are counted for this model with the
+    library's own buffer-size helpers, fp32 scales included."""
+    zero3 = 3 * 2 * M
+    zeropp = (M + 4 * zq.num_blocks(M, 2048)) + (zq.int4_code_bytes(M) + 4 * zq.num_blocks(M, 128))
+    return {
+        "note": "context only, not a target",
+        "comm_bytes_per_step_7.5B": {"zero3": zero3, "zeropp_int8_w2048_int4_g128": zeropp,
+                                     "ratio": round(zero3 / zeropp, 3),
+                                     "pages": "3M -> 0.75M in fp16 units (4x), scales not counted"},
+        "zeropp_throughput_vs_zero": "2.16x at 384 GPUs (GPU model and workload not stated)",
+    }
 
 
 def ceilings(torch, dev):
