@@ -37,21 +37,33 @@ namespace {
 #ifndef ZQ_DR_VEC_RQ
 #define ZQ_DR_VEC_RQ 8
 #endif
+// With requant EF (two more fp32 streams per output) 4 outputs per lane per
+// sub-vector measured best: 1.96 against 2.16 ms at 7.5B / 8 peers, while
+// the requant without EF is issue-bound and prefers 8 (0.97 against 1.23 ms).
+#ifndef ZQ_DR_VEC_RQEF
+#define ZQ_DR_VEC_RQEF 4
+#endif
+#ifndef ZQ_DR_U_RQEF
+#define ZQ_DR_U_RQEF ZQ_DR_U
+#endif
 
-template <int B, int V>
+template <int B, int V, int UB>
 struct DrGeom {
     static constexpr int VEC = V;
     static constexpr int SUB = kWave * VEC;
     static constexpr int LPB = B <= SUB ? B / VEC : kWave;
     static constexpr int SPB = B <= SUB ? 1 : B / SUB;
-    static constexpr int U0 = ZQ_DR_U * 8 / VEC;
+    static constexpr int U0 = UB * 8 / VEC;
     static constexpr int U = SPB > U0 ? SPB : U0;
     static constexpr int TILE = SUB * U;
     static constexpr int BPT = TILE / B;
 };
 
-template <bool RQ>
-constexpr int dr_vec() { return RQ ? ZQ_DR_VEC_RQ : ZQ_DR_VEC_OUT; }
+// Tile geometry of each kernel flavour: fp32 output only, requant, requant
+// with its error-feedback buffer.
+template <int B, bool RQ, bool EF>
+using DrGeomOf = DrGeom<B, RQ ? (EF ? ZQ_DR_VEC_RQEF : ZQ_DR_VEC_RQ) : ZQ_DR_VEC_OUT,
+                        RQ && EF ? ZQ_DR_U_RQEF : ZQ_DR_U>;
 
 template <int V>
 using code_word_t = typename std::conditional<V == 8, uint32_t, uint16_t>::type;
@@ -119,11 +131,11 @@ __device__ __forceinline__ uint32_t load_code_word_masked(const uint8_t* p, size
     return w;
 }
 
-template <int B, int PMAX, bool OUT, bool RQ, bool MASK>
+template <int B, int PMAX, bool OUT, bool RQ, bool EF, bool MASK>
 __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
-    const bool RQEF = RQ && p.rq_ef != nullptr;
-    constexpr int V = dr_vec<RQ>();
-    using G = DrGeom<B, V>;
+    constexpr bool RQEF = RQ && EF;  // requant with its EF buffer (p.rq_ef)
+    using G = DrGeomOf<B, RQ, EF>;
+    constexpr int V = G::VEC;
     const int lane = lane_id();
     const size_t base = tile * (size_t)G::TILE;
     const size_t n = p.n;
@@ -150,7 +162,7 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
             }
         }
     }
-    if (RQEF) {
+    if constexpr (RQEF) {
 #pragma unroll
         for (int u = 0; u < G::U; ++u) {
             const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
@@ -218,7 +230,7 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
     if constexpr (RQ) {
         // Compensated requant input, in place (R is not needed any more).
         float (&c)[G::U][V] = R;
-        if (RQEF) {
+        if constexpr (RQEF) {
 #pragma unroll
             for (int u = 0; u < G::U; ++u)
 #pragma unroll
@@ -297,7 +309,7 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
 #pragma unroll
             for (int u = 0; u < G::U; ++u) {
                 packed[u] = pack_nibbles_f<V>(kf[u]);
-                if (RQEF) {
+                if constexpr (RQEF) {
                     const BlockScale& b = bs[G::SPB == 1 ? u : u / G::SPB];
 #pragma unroll
                     for (int j = 0; j < V; ++j)
@@ -314,7 +326,7 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
                 for (int j = 0; j < V; ++j) {
                     const int k = code_clamp<7>(code_fix<7>(c[u][j], b, kf[u][j]));
                     packed[u] |= ((uint32_t)k & 0xFu) << (4 * j);
-                    if (RQEF)
+                    if constexpr (RQEF)
                         e2[u][j] = ef_update(c[u][j], k, b.s, e2[u][j], p.rq_beta_e, p.rq_beta_r);
                 }
             }
@@ -324,7 +336,7 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
             const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
             if constexpr (!MASK) {
                 st_stream((code_word_t<V>)packed[u], (code_word_t<V>*)(p.rq_codes + i0 / 2));
-                if (RQEF) {
+                if constexpr (RQEF) {
 #pragma unroll
                     for (int h = 0; h < V / 4; ++h) {
                         const f4 a = {e2[u][4 * h], e2[u][4 * h + 1], e2[u][4 * h + 2],
@@ -337,7 +349,7 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
                 for (int b = 0; b < V / 2; ++b)
                     if (i0 + 2 * b < n)
                         p.rq_codes[i0 / 2 + b] = (uint8_t)(packed[u] >> (8 * b));
-                if (RQEF) {
+                if constexpr (RQEF) {
 #pragma unroll
                     for (int j = 0; j < V; ++j)
                         if (i0 + j < n)
@@ -351,48 +363,50 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
 // PMAX: the kernel serves every P <= PMAX; only PMAX pointer pairs stay
 // live, so the common P = 4 / 8 cases keep their pointers in SGPRs.  Full
 // tiles only; the ragged last tile is a second one-wave launch (MASK).
-template <int B, int PMAX, bool OUT, bool RQ, bool MASK>
+template <int B, int PMAX, bool OUT, bool RQ, bool EF, bool MASK>
 __global__ __launch_bounds__(kBlockThreads) void dr_kernel(DrParams p) {
-    using G = DrGeom<B, dr_vec<RQ>()>;
+    using G = DrGeomOf<B, RQ, EF>;
     if constexpr (MASK) {
-        dr_tile<B, PMAX, OUT, RQ, true>(p, p.n / G::TILE);
+        dr_tile<B, PMAX, OUT, RQ, EF, true>(p, p.n / G::TILE);
     } else {
         const size_t nfull = p.n / G::TILE;
         // Plain dispatch order: the XCD-contiguous order of the streaming
         // kernels measured slower here (P peer streams per XCD run).
         for (size_t t = wave_id(); t < nfull; t += wave_count())
-            dr_tile<B, PMAX, OUT, RQ, false>(p, t);
+            dr_tile<B, PMAX, OUT, RQ, EF, false>(p, t);
     }
 }
 
-template <int B, int PMAX, bool OUT, bool RQ>
+template <int B, int PMAX, bool OUT, bool RQ, bool EF>
 hipError_t launch_b(const DrParams& p, hipStream_t stream) {
-    using G = DrGeom<B, dr_vec<RQ>()>;
+    using G = DrGeomOf<B, RQ, EF>;
     const size_t nfull = p.n / G::TILE;
     DrParams arg = p;
     void* args[] = {(void*)&arg};
     // Requant without EF keeps a persistent grid; with EF (two more fp32
     // streams) one tile per wave keeps more bytes in flight and is faster.
-    const Geometry geom = (RQ && p.rq_ef == nullptr) ? kGeomReduceRequant : kGeomReduce;
+    const Geometry geom = (RQ && !EF) ? kGeomReduceRequant : kGeomReduce;
     hipError_t e = hipSuccess;
     if (nfull)
-        e = hipLaunchKernel((const void*)&dr_kernel<B, PMAX, OUT, RQ, false>,
+        e = hipLaunchKernel((const void*)&dr_kernel<B, PMAX, OUT, RQ, EF, false>,
                             grid_for_tiles(nfull, geom), dim3(geom.threads), args, 0, stream);
     if (e == hipSuccess && p.n % G::TILE)
-        e = hipLaunchKernel((const void*)&dr_kernel<B, PMAX, OUT, RQ, true>, dim3(1), dim3(kWave),
-                            args, 0, stream);
+        e = hipLaunchKernel((const void*)&dr_kernel<B, PMAX, OUT, RQ, EF, true>, dim3(1),
+                            dim3(kWave), args, 0, stream);
     return e;
 }
 
 template <int B, int PMAX>
 hipError_t launch_flags(const DrParams& p, hipStream_t st) {
-    const bool out = p.out != nullptr, rq = p.rq_codes != nullptr;
+    const bool out = p.out != nullptr, rq = p.rq_codes != nullptr, ef = p.rq_ef != nullptr;
     if (out && !rq)
-        return launch_b<B, PMAX, true, false>(p, st);
+        return launch_b<B, PMAX, true, false, false>(p, st);
     if (!out && rq)
-        return launch_b<B, PMAX, false, true>(p, st);
+        return ef ? launch_b<B, PMAX, false, true, true>(p, st)
+                  : launch_b<B, PMAX, false, true, false>(p, st);
     if (out && rq)
-        return launch_b<B, PMAX, true, true>(p, st);
+        return ef ? launch_b<B, PMAX, true, true, true>(p, st)
+                  : launch_b<B, PMAX, true, true, false>(p, st);
     return hipErrorInvalidValue;
 }
 
