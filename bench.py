@@ -111,8 +111,8 @@ def main():
         kernel_table()
         return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU exchange (RCCL all-to-all over xGMI) is not part of it.",
+        print(f"bench.py: libzq measures one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU exchange (RCCL all-to-all over xGMI) is not implemented.",
               file=sys.stderr)
         sys.exit(2)
 
