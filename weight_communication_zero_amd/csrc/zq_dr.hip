@@ -46,6 +46,9 @@ namespace {
 #ifndef ZQ_DR_U_RQEF
 #define ZQ_DR_U_RQEF ZQ_DR_U
 #endif
+#ifndef ZQ_DR_U_RQ
+#define ZQ_DR_U_RQ ZQ_DR_U
+#endif
 
 template <int B, int V, int UB>
 struct DrGeom {
@@ -63,7 +66,7 @@ struct DrGeom {
 // with its error-feedback buffer.
 template <int B, bool RQ, bool EF>
 using DrGeomOf = DrGeom<B, RQ ? (EF ? ZQ_DR_VEC_RQEF : ZQ_DR_VEC_RQ) : ZQ_DR_VEC_OUT,
-                        RQ && EF ? ZQ_DR_U_RQEF : ZQ_DR_U>;
+                        RQ ? (EF ? ZQ_DR_U_RQEF : ZQ_DR_U_RQ) : ZQ_DR_U>;
 
 template <int V>
 using code_word_t = typename std::conditional<V == 8, uint32_t, uint16_t>::type;
