@@ -1,498 +1,20 @@
-// zq_dr.hip -- qgZ receive side: dequantize P int4 chunks, reduce in fp32,
-// optionally requantize (with optional error feedback) for the next level.
-//
-// Definition ("ZeROPlusPlus.md" notes, section 1.2: gradients travel as
-// block int4 through an all-to-all, the reduction is done back in full
-// precision, inside the node first and then across nodes, with fused
-// kernels to cut latency):
-//   S = d_0 + d_1 + ... + d_{P-1}   (left to right, d_p = fl(k_p s_p))
-//   R = alpha * S;  out = R;  requant: the EF int4 quantizer applied to R.
-//
-// One pass: P * (0.5 B + 4/B B) read per output element, 4 B written when
-// out is requested, 0.5 B + 4/B B (+8 B with requant EF) for the requant.
-// In sub-vector u lane l owns the 8 outputs starting at u*512 + 8l, i.e. one
-// 32-bit word of codes per peer: each code load instruction of the wave
-// reads 256 contiguous bytes.  The sum order is fixed (ascending peer), so
-// the fp32 sums -- and the requant codes that depend on their exact bits --
-// are deterministic.  No LDS.
-#include <type_traits>
-
-#include "zq_device.h"
-#include "zq_launch.h"
-
-#ifndef ZQ_DR_U
-#define ZQ_DR_U 2  // sub-vectors of 512 outputs per wave tile
-#endif
+// zq_dr.hip -- entry of the dequantize-reduce(-requant) launch: picks the
+// launcher of the block size.  The kernels live in zq_dr_kernels.h; each
+// block size's instantiations are compiled in zq_dr_b*.hip.
+#include "zq_dr_launch.h"
 
 namespace zq {
-namespace {
-
-// VEC outputs per lane per sub-vector: 8 (one 32-bit code word per peer,
-// two 16-byte output stores per lane) or 4 (one 16-bit code word per peer,
-// one 16-byte store per lane, so each store instruction writes 1 KB
-// contiguously).  Both keep 16 outputs per lane per tile.
-#ifndef ZQ_DR_VEC_OUT
-#define ZQ_DR_VEC_OUT 4
-#endif
-#ifndef ZQ_DR_VEC_RQ
-#define ZQ_DR_VEC_RQ 8
-#endif
-// With requant EF (two more fp32 streams per output) 4 outputs per lane per
-// sub-vector measured best: 1.96 against 2.16 ms at 7.5B / 8 peers, while
-// the requant without EF is issue-bound and prefers 8 (0.97 against 1.23 ms).
-#ifndef ZQ_DR_VEC_RQEF
-#define ZQ_DR_VEC_RQEF 4
-#endif
-#ifndef ZQ_DR_U_RQEF
-#define ZQ_DR_U_RQEF ZQ_DR_U
-#endif
-#ifndef ZQ_DR_U_RQ
-#define ZQ_DR_U_RQ ZQ_DR_U
-#endif
-
-template <int B, int V, int UB>
-struct DrGeom {
-    static constexpr int VEC = V;
-    static constexpr int SUB = kWave * VEC;
-    static constexpr int LPB = B <= SUB ? B / VEC : kWave;
-    static constexpr int SPB = B <= SUB ? 1 : B / SUB;
-    static constexpr int U0 = UB * 8 / VEC;
-    static constexpr int U = SPB > U0 ? SPB : U0;
-    static constexpr int TILE = SUB * U;
-    static constexpr int BPT = TILE / B;
-};
-
-// Tile geometry of each kernel flavour: fp32 output only, requant, requant
-// with its error-feedback buffer.
-template <int B, bool RQ, bool EF>
-using DrGeomOf = DrGeom<B, RQ ? (EF ? ZQ_DR_VEC_RQEF : ZQ_DR_VEC_RQ) : ZQ_DR_VEC_OUT,
-                        RQ ? (EF ? ZQ_DR_U_RQEF : ZQ_DR_U_RQ) : ZQ_DR_U>;
-
-template <int V>
-using code_word_t = typename std::conditional<V == 8, uint32_t, uint16_t>::type;
-
-// Signed value of nibble j of a code word (shift it to the top, then an
-// arithmetic shift back down sign-extends it).
-__device__ __forceinline__ float nib(uint32_t w, int j) {
-    return (float)((int32_t)(w << (28 - 4 * j)) >> 28);
-}
-
-// Same rounding as code_fast, by the addition of 1.5 * 2^23: for |y| < 2^22
-// the sum lies in [2^23, 2^24), where the fp32 spacing is 1, so it rounds y
-// half-to-even onto the integers (1.5 * 2^23 is even) and the subtraction
-// recovers rne(y) exactly -- as +0 where rintf gives -0, which the integer
-// code does not see.  The caller guarantees a finite block scale, so
-// |y| <= qmax (1 + 2^-22) unless `redo` is set anyway.
-template <int QMAX>
-__device__ __forceinline__ float code_fast_rne(float x, const BlockScale& b, bool& redo) {
-    const float y = x * b.inv;
-    const float k = (y + 0x1.8p23f) - 0x1.8p23f;
-    redo |= __builtin_fabsf(y - k) > tie_band<QMAX>();
-    return k;
-}
-
-// Two's-complement nibbles of V (4 or 8) integer-valued floats in [-7, 7],
-// element j in bits 4j..4j+3.  Per group of four the biased digits k_j + 8
-// lie in [1, 15], so W = sum (k_j + 8) 16^j has no carries between digits;
-// it is an integer below 2^16, exact in fp32, and adding 1.5 * 2^23 puts it
-// in the low mantissa bits (the bias 0x8888 rides on that constant).
-// Flipping bit 3 of every digit (xor 0x8...8) then gives k_j mod 16.  The
-// two groups of eight are joined by a byte permute.
-template <int V>
-__device__ __forceinline__ uint32_t pack_nibbles_f(const float (&k)[V]) {
-    uint32_t h[2];
-#pragma unroll
-    for (int g = 0; g < V / 4; ++g) {
-        const float lo = __builtin_fmaf(k[4 * g + 1], 16.0f, k[4 * g]);
-        const float hi = __builtin_fmaf(k[4 * g + 3], 16.0f, k[4 * g + 2]);
-        h[g] = fbits(__builtin_fmaf(hi, 256.0f, lo) + (0x1.8p23f + (float)0x8888));
-    }
-    if constexpr (V == 8)
-        return __builtin_amdgcn_perm(h[1], h[0], 0x05040100u) ^ 0x88888888u;
-    else
-        return (h[0] ^ 0x8888u) & 0xFFFFu;
-}
-
-// ef_update with the code given as an exact integer-valued float (+0 for 0).
-__device__ __forceinline__ float ef_update_f(float c, float k, float s, float e, float be, float br) {
-    float d = k * s;
-    float r = c - d;
-    float t1 = be * e;
-    float t2 = br * r;
-    return t1 + t2;
-}
-
-// Wave-uniform copy of a value that every lane holds, in scalar registers.
-__device__ __forceinline__ size_t uniform64(size_t x) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
-    return ((size_t)hi << 32) | lo;
-}
-
-// Buffer addressing for the issue-bound requant without EF: every stream of
-// a full tile is read and written through a raw buffer resource built in
-// scalar registers from the tile's base address, with a 32-bit per-lane
-// byte offset, so no 64-bit address arithmetic runs on the vector ALU.  The
-// resource spans the tile's bytes of that stream (the offsets stay inside).
-// Word 3 is the gfx9-family raw-buffer format word; cache-policy bit 1 is
-// the nontemporal hint.  Measured A/B in one process at 7.5B / 8 peers:
-// 1.027 -> 0.969 ms for this kernel, while the fp32-out reduce (+1.6 %) and
-// the requant with EF (equal) keep plain global accesses.
-template <typename T, int POLICY>
-__device__ __forceinline__ T buf_load(const void* base, uint32_t bytes, uint32_t off) {
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-    if constexpr (sizeof(T) == 2)
-        return __builtin_bit_cast(T, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, POLICY));
-    else if constexpr (sizeof(T) == 4)
-        return __builtin_bit_cast(T, (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, POLICY));
-    else
-        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY));
-}
-template <typename T, int POLICY>
-__device__ __forceinline__ void buf_store(T v, void* base, uint32_t bytes, uint32_t off) {
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
-    if constexpr (sizeof(T) == 2)
-        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), r, off, 0, POLICY);
-    else if constexpr (sizeof(T) == 4)
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, POLICY);
-    else
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, POLICY);
-}
-constexpr int kBufLoadNT = ZQ_NT_LOAD ? 2 : 0;
-constexpr int kBufStoreNT = ZQ_NT_STORE ? 2 : 0;
-
-// Up to NB code bytes starting at byte offset ob, only those below nbytes.
-template <int NB>
-__device__ __forceinline__ uint32_t load_code_word_masked(const uint8_t* p, size_t ob,
-                                                          size_t nbytes) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-        if (ob + b < nbytes)
-            w |= (uint32_t)p[ob + b] << (8 * b);
-    return w;
-}
-
-template <int B, int PMAX, bool OUT, bool RQ, bool EF, bool MASK>
-__device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
-    constexpr bool RQEF = RQ && EF;  // requant with its EF buffer (p.rq_ef)
-    using G = DrGeomOf<B, RQ, EF>;
-    constexpr int V = G::VEC;
-    constexpr bool BUF = RQ && !EF && !MASK;  // buffer addressing (see buf_load)
-    const int lane = lane_id();
-    const size_t base = (BUF ? uniform64(tile) : tile) * (size_t)G::TILE;
-    const size_t n = p.n;
-    const size_t nbytes = (n + 1) / 2;
-
-    uint32_t cw[PMAX][G::U];  // code words (VEC nibbles each)
-    float sc[PMAX][G::U];
-    float e2[G::U][V];
-
-    // Issue every load of the tile first.
-#pragma unroll
-    for (int q = 0; q < PMAX; ++q) {
-        if (q < (int)p.P) {
-#pragma unroll
-            for (int u = 0; u < G::U; ++u) {
-                const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
-                if constexpr (BUF) {
-                    const uint32_t le = (uint32_t)(u * G::SUB + lane * V);
-                    cw[q][u] = buf_load<code_word_t<V>, kBufLoadNT>(p.codes[q] + base / 2,
-                                                                    G::TILE / 2, le / 2);
-                    sc[q][u] = buf_load<float, 0>(p.scales[q] + base / B, G::TILE / B * 4,
-                                                  4u * (le / B));
-                } else if constexpr (!MASK) {
-                    cw[q][u] = ld_stream((const code_word_t<V>*)(p.codes[q] + i0 / 2));
-                    sc[q][u] = p.scales[q][i0 / B];
-                } else {
-                    cw[q][u] = load_code_word_masked<V / 2>(p.codes[q], i0 / 2, nbytes);
-                    sc[q][u] = i0 < n ? p.scales[q][i0 / B] : 0.0f;
-                }
-            }
-        }
-    }
-    if constexpr (RQEF) {
-#pragma unroll
-        for (int u = 0; u < G::U; ++u) {
-            const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
-            if constexpr (!MASK) {
-#pragma unroll
-                for (int h = 0; h < V / 4; ++h) {
-                    const f4 a = ld_stream((const f4*)(p.rq_ef + i0 + 4 * h));
-                    e2[u][4 * h] = a.x; e2[u][4 * h + 1] = a.y;
-                    e2[u][4 * h + 2] = a.z; e2[u][4 * h + 3] = a.w;
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < V; ++j)
-                    e2[u][j] = i0 + j < n ? p.rq_ef[i0 + j] : 0.0f;
-            }
-        }
-    }
-
-    // Dequantize and reduce, ascending peer order.  Peers are the outer loop
-    // so the runtime test q < P is one uniform branch per peer, not a select
-    // per element; alpha = 1 is skipped (multiplying by one is the identity).
-    float R[G::U][V];
-#pragma unroll
-    for (int u = 0; u < G::U; ++u)
-#pragma unroll
-        for (int j = 0; j < V; ++j)
-            R[u][j] = nib(cw[0][u], j) * sc[0][u];
-#pragma unroll
-    for (int q = 1; q < PMAX; ++q) {
-        if (q < (int)p.P) {
-#pragma unroll
-            for (int u = 0; u < G::U; ++u)
-#pragma unroll
-                for (int j = 0; j < V; ++j)
-                    R[u][j] = R[u][j] + nib(cw[q][u], j) * sc[q][u];
-        }
-    }
-    if (p.alpha != 1.0f) {
-#pragma unroll
-        for (int u = 0; u < G::U; ++u)
-#pragma unroll
-            for (int j = 0; j < V; ++j)
-                R[u][j] = p.alpha * R[u][j];
-    }
-
-    if constexpr (OUT) {
-#pragma unroll
-        for (int u = 0; u < G::U; ++u) {
-            const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
-            if constexpr (!MASK) {
-#pragma unroll
-                for (int h = 0; h < V / 4; ++h) {
-                    const f4 a = {R[u][4 * h], R[u][4 * h + 1], R[u][4 * h + 2], R[u][4 * h + 3]};
-                    if constexpr (BUF)
-                        buf_store<f4, kBufStoreNT>(a, p.out + base, G::TILE * 4,
-                                                   4u * (uint32_t)(u * G::SUB + lane * V + 4 * h));
-                    else
-                        st_stream(a, (f4*)(p.out + i0 + 4 * h));
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < V; ++j)
-                    if (i0 + j < n)
-                        p.out[i0 + j] = R[u][j];
-            }
-        }
-    }
-
-    if constexpr (RQ) {
-        // Compensated requant input, in place (R is not needed any more).
-        float (&c)[G::U][V] = R;
-        if constexpr (RQEF) {
-#pragma unroll
-            for (int u = 0; u < G::U; ++u)
-#pragma unroll
-                for (int j = 0; j < V; ++j)
-                    c[u][j] = R[u][j] + e2[u][j];
-        }
-        // Beyond n the value must not enter the block max.
-        if constexpr (MASK) {
-#pragma unroll
-            for (int u = 0; u < G::U; ++u) {
-                const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
-#pragma unroll
-                for (int j = 0; j < V; ++j)
-                    if (i0 + j >= n)
-                        c[u][j] = 0.0f;
-            }
-        }
-        BlockScale bs[G::SPB == 1 ? G::U : G::BPT];
-        if constexpr (G::SPB == 1) {
-#pragma unroll
-            for (int u = 0; u < G::U; ++u) {
-                uint32_t m = 0;
-#pragma unroll
-                for (int j = 0; j < V; ++j)
-                    m = max(m, absbits(c[u][j]));
-                bs[u] = block_scale<7>(group_max<G::LPB>(m));
-            }
-        } else {
-#pragma unroll
-            for (int b = 0; b < G::BPT; ++b) {
-                uint32_t m = 0;
-#pragma unroll
-                for (int u = b * G::SPB; u < (b + 1) * G::SPB; ++u)
-#pragma unroll
-                    for (int j = 0; j < V; ++j)
-                        m = max(m, absbits(c[u][j]));
-                bs[b] = block_scale<7>(group_max<kWave>(m));
-            }
-        }
-        if constexpr (G::SPB == 1) {
-            if (lane % G::LPB == 0) {
-#pragma unroll
-                for (int u = 0; u < G::U; ++u) {
-                    const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
-                    if (!MASK || i0 < n)
-                        p.rq_scales[i0 / B] = bs[u].s;
-                }
-            }
-        } else {
-            if (lane == 0) {
-#pragma unroll
-                for (int b = 0; b < G::BPT; ++b) {
-                    const size_t i0 = base + (size_t)b * B;
-                    if (!MASK || i0 < n)
-                        p.rq_scales[i0 / B] = bs[b].s;
-                }
-            }
-        }
-        // Fast codes: rne(c * rcp(s)) by the 1.5 * 2^23 addition.  A tile
-        // falls back to the IEEE quotient when an element is in the tie band
-        // or a block scale is subnormal, infinite or NaN (uniform branch).
-        float kf[G::U][V];
-        bool redo = false;
-#pragma unroll
-        for (int u = 0; u < G::U; ++u) {
-            const BlockScale& b = bs[G::SPB == 1 ? u : u / G::SPB];
-            redo |= b.exact | !(b.s <= 0x1.fffffep127f);
-#pragma unroll
-            for (int j = 0; j < V; ++j)
-                kf[u][j] = code_fast_rne<7>(c[u][j], b, redo);
-        }
-        uint32_t packed[G::U];
-        if (__builtin_amdgcn_ballot_w64(redo) == 0) {
-            // Every |code| <= 7 here: pack the float codes, and use them as
-            // exact integers in the error feedback.
-#pragma unroll
-            for (int u = 0; u < G::U; ++u) {
-                packed[u] = pack_nibbles_f<V>(kf[u]);
-                if constexpr (RQEF) {
-                    const BlockScale& b = bs[G::SPB == 1 ? u : u / G::SPB];
-#pragma unroll
-                    for (int j = 0; j < V; ++j)
-                        e2[u][j] = ef_update_f(c[u][j], kf[u][j], b.s, e2[u][j], p.rq_beta_e,
-                                               p.rq_beta_r);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < G::U; ++u) {
-                const BlockScale& b = bs[G::SPB == 1 ? u : u / G::SPB];
-                packed[u] = 0;
-#pragma unroll
-                for (int j = 0; j < V; ++j) {
-                    const int k = code_clamp<7>(code_fix<7>(c[u][j], b, kf[u][j]));
-                    packed[u] |= ((uint32_t)k & 0xFu) << (4 * j);
-                    if constexpr (RQEF)
-                        e2[u][j] = ef_update(c[u][j], k, b.s, e2[u][j], p.rq_beta_e, p.rq_beta_r);
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < G::U; ++u) {
-            const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
-            if constexpr (!MASK) {
-                if constexpr (BUF)
-                    buf_store<code_word_t<V>, kBufStoreNT>((code_word_t<V>)packed[u],
-                                                           p.rq_codes + base / 2, G::TILE / 2,
-                                                           (uint32_t)(u * G::SUB + lane * V) / 2);
-                else
-                    st_stream((code_word_t<V>)packed[u], (code_word_t<V>*)(p.rq_codes + i0 / 2));
-                if constexpr (RQEF) {
-#pragma unroll
-                    for (int h = 0; h < V / 4; ++h) {
-                        const f4 a = {e2[u][4 * h], e2[u][4 * h + 1], e2[u][4 * h + 2],
-                                      e2[u][4 * h + 3]};
-                        st_stream(a, (f4*)(p.rq_ef + i0 + 4 * h));
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int b = 0; b < V / 2; ++b)
-                    if (i0 + 2 * b < n)
-                        p.rq_codes[i0 / 2 + b] = (uint8_t)(packed[u] >> (8 * b));
-                if constexpr (RQEF) {
-#pragma unroll
-                    for (int j = 0; j < V; ++j)
-                        if (i0 + j < n)
-                            p.rq_ef[i0 + j] = e2[u][j];
-                }
-            }
-        }
-    }
-}
-
-// PMAX: the kernel serves every P <= PMAX; only PMAX pointer pairs stay
-// live, so the common P = 4 / 8 cases keep their pointers in SGPRs.  Full
-// tiles only; the ragged last tile is a second one-wave launch (MASK).
-template <int B, int PMAX, bool OUT, bool RQ, bool EF, bool MASK>
-__global__ __launch_bounds__(kBlockThreads) void dr_kernel(DrParams p) {
-    using G = DrGeomOf<B, RQ, EF>;
-    if constexpr (MASK) {
-        dr_tile<B, PMAX, OUT, RQ, EF, true>(p, p.n / G::TILE);
-    } else {
-        const size_t nfull = p.n / G::TILE;
-        // Plain dispatch order: the XCD-contiguous order of the streaming
-        // kernels measured slower here (P peer streams per XCD run).
-        for (size_t t = wave_id(); t < nfull; t += wave_count())
-            dr_tile<B, PMAX, OUT, RQ, EF, false>(p, t);
-    }
-}
-
-template <int B, int PMAX, bool OUT, bool RQ, bool EF>
-hipError_t launch_b(const DrParams& p, hipStream_t stream) {
-    using G = DrGeomOf<B, RQ, EF>;
-    const size_t nfull = p.n / G::TILE;
-    DrParams arg = p;
-    void* args[] = {(void*)&arg};
-    // Requant without EF keeps a persistent grid; with EF (two more fp32
-    // streams) one tile per wave keeps more bytes in flight and is faster.
-    const Geometry geom = (RQ && !EF) ? kGeomReduceRequant : kGeomReduce;
-    hipError_t e = hipSuccess;
-    if (nfull)
-        e = hipLaunchKernel((const void*)&dr_kernel<B, PMAX, OUT, RQ, EF, false>,
-                            grid_for_tiles(nfull, geom), dim3(geom.threads), args, 0, stream);
-    if (e == hipSuccess && p.n % G::TILE)
-        e = hipLaunchKernel((const void*)&dr_kernel<B, PMAX, OUT, RQ, EF, true>, dim3(1),
-                            dim3(kWave), args, 0, stream);
-    return e;
-}
-
-template <int B, int PMAX>
-hipError_t launch_flags(const DrParams& p, hipStream_t st) {
-    const bool out = p.out != nullptr, rq = p.rq_codes != nullptr, ef = p.rq_ef != nullptr;
-    if (out && !rq)
-        return launch_b<B, PMAX, true, false, false>(p, st);
-    if (!out && rq)
-        return ef ? launch_b<B, PMAX, false, true, true>(p, st)
-                  : launch_b<B, PMAX, false, true, false>(p, st);
-    if (out && rq)
-        return ef ? launch_b<B, PMAX, true, true, true>(p, st)
-                  : launch_b<B, PMAX, true, true, false>(p, st);
-    return hipErrorInvalidValue;
-}
-
-template <int B>
-hipError_t launch_peers(const DrParams& p, hipStream_t st) {
-    if (p.P <= 2)
-        return launch_flags<B, 2>(p, st);
-    if (p.P <= 4)
-        return launch_flags<B, 4>(p, st);
-    if (p.P <= 8)
-        return launch_flags<B, 8>(p, st);
-    return launch_flags<B, 16>(p, st);
-}
-
-}  // namespace
 
 hipError_t launch_dequant_reduce(const DrParams& p, uint32_t block, hipStream_t st) {
     switch (block) {
-        case 32: return launch_peers<32>(p, st);
-        case 64: return launch_peers<64>(p, st);
-        case 128: return launch_peers<128>(p, st);
-        case 256: return launch_peers<256>(p, st);
-        case 512: return launch_peers<512>(p, st);
-        case 1024: return launch_peers<1024>(p, st);
-        case 2048: return launch_peers<2048>(p, st);
-        case 4096: return launch_peers<4096>(p, st);
+        case 32: return launch_dr_b32(p, st);
+        case 64: return launch_dr_b64(p, st);
+        case 128: return launch_dr_b128(p, st);
+        case 256: return launch_dr_b256(p, st);
+        case 512: return launch_dr_b512(p, st);
+        case 1024: return launch_dr_b1024(p, st);
+        case 2048: return launch_dr_b2048(p, st);
+        case 4096: return launch_dr_b4096(p, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -1,0 +1,10 @@
+// zq_dr_b128_256.hip -- dequantize-reduce(-requant) kernels for blocks of
+// 128 and 256 elements (see zq_dr_kernels.h).
+#include "zq_dr_kernels.h"
+
+namespace zq {
+
+ZQ_DR_LAUNCHER(128)
+ZQ_DR_LAUNCHER(256)
+
+}  // namespace zq
