@@ -258,7 +258,8 @@ def extreme_scale_chunks(P, n, block, seed, top):
 
 
 @pytest.mark.parametrize("block", [32, 128, 1024, 4096])
-@pytest.mark.parametrize("flags", [(True, False, False), (False, True, False), (True, True, True)])
+@pytest.mark.parametrize("flags", [(True, False, False), (False, True, False), (False, True, True),
+                                   (True, True, True)])
 def test_dequant_reduce_extreme_scales(block, flags):
     want_out, requant, rqef = flags
     n = max(1024, block) * 9 + 3
@@ -269,6 +270,29 @@ def test_dequant_reduce_extreme_scales(block, flags):
                  chunks=extreme_scale_chunks(P, n, block, block + P, top=30))
     check_dr(1, n, block, 1.0, want_out, requant, rqef, seed=block,
              chunks=extreme_scale_chunks(1, n, block, block, top=124.99))
+
+
+@pytest.mark.parametrize("with_rq_ef", [False, True])
+def test_requant_scales_at_the_decode_boundary(with_rq_ef):
+    """8 peers of moderate scales, and in chosen tiles one peer whose block
+    scale is 2^124 or 1.5 * 2^124 (the requant kernels then redo that tile
+    from the integer nibbles) or the float just below 2^124 (still the k / 16
+    decode).  Every sum stays finite, as the contract asks."""
+    P, B = 8, 128
+    n = 1024 * 8 + 130
+    codes, scales = make_chunks(P, n, B, seed=77, raw=True)
+    for s in scales:
+        s[:] = np.abs(s)
+    big = np.float32(2.0 ** 124)
+    # (block, peer, scale): one huge scale per block, so no sum overflows;
+    # blocks 64 and 65 are the ragged tail
+    placed = [(11, 3, big), (19, 5, np.nextafter(big, np.float32(0))), (27, 0, big),
+              (28, 7, np.float32(2.0 ** 124 * 1.5)), (35, 2, np.nextafter(big, np.float32(0))),
+              (51, 4, big), (65, 1, big)]
+    for b, peer, v in placed:
+        scales[peer][b] = v
+    check_dr(P, n, B, 1.0, False, True, with_rq_ef, seed=78, chunks=(codes, scales))
+    check_dr(P, n, B, 1.0, True, True, with_rq_ef, seed=79, chunks=(codes, scales))
 
 
 # ---------------------------------------------------------------- qwZ int8 --

@@ -80,6 +80,39 @@ __device__ __forceinline__ float nib(uint32_t w, int j) {
     return (float)((int32_t)(w << (28 - 4 * j)) >> 28);
 }
 
+// The same nibbles divided by 16, from gfx950's v_cvt_off_f32_i4: it reads
+// bits [3:0] of its operand as a two's-complement int4 k and returns k / 16,
+// which is exact.  Even nibbles are the low halves of the word's bytes, odd
+// nibbles those of the word shifted right by 4, and the instruction's operand
+// byte select picks the byte, so V nibbles cost V conversions and one shift
+// (the empty asm hides the shifted word from the compiler, which would
+// otherwise fold the shift into a bit-field extract per nibble).  With
+// t = fl(16 s) finite, fl((k / 16) t) = fl(k s) bit for bit: both factors are
+// exact and their exact product is k s.  Measured A/B in one process at 7.5B
+// / 8 peers, requant without EF: 0.946 -> 0.922 ms; the fp32-out reduce
+// gained nothing and keeps the integer decode (ZQ_DR_DECODE_OFF=0 turns the
+// k / 16 decode off everywhere).
+#ifndef ZQ_DR_DECODE_OFF
+#define ZQ_DR_DECODE_OFF 1
+#endif
+__device__ __forceinline__ float off4(uint32_t v) { return __builtin_amdgcn_cvt_off_f32_i4((int)v); }
+
+template <int V>
+__device__ __forceinline__ void nib16(uint32_t w, float (&f)[V]) {
+    uint32_t y = w >> 4;
+    asm("" : "+v"(y));
+    f[0] = off4(w);
+    f[1] = off4(y);
+    f[2] = off4((w >> 8) & 0xFFu);
+    f[3] = off4((y >> 8) & 0xFFu);
+    if constexpr (V == 8) {
+        f[4] = off4((w >> 16) & 0xFFu);
+        f[5] = off4((y >> 16) & 0xFFu);
+        f[6] = off4(w >> 24);
+        f[7] = off4(y >> 24);
+    }
+}
+
 // Same rounding as code_fast, by the addition of 1.5 * 2^23: for |y| < 2^22
 // the sum lies in [2^23, 2^24), where the fp32 spacing is 1, so it rounds y
 // half-to-even onto the integers (1.5 * 2^23 is even) and the subtraction
@@ -178,22 +211,17 @@ __device__ __forceinline__ uint32_t load_code_word_masked(const uint8_t* p, size
     return w;
 }
 
-template <int B, int PMAX, bool OUT, bool RQ, bool EF, bool MASK>
-__device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
-    constexpr bool RQEF = RQ && EF;  // requant with its EF buffer (p.rq_ef)
+// The code words and scales of every peer for one tile (see dr_tile).
+template <int B, int PMAX, bool RQ, bool EF, bool MASK>
+__device__ __forceinline__ void dr_load(const DrParams& p, size_t base,
+                                        uint32_t (&cw)[PMAX][DrGeomOf<B, RQ, EF>::U],
+                                        float (&sc)[PMAX][DrGeomOf<B, RQ, EF>::U]) {
     using G = DrGeomOf<B, RQ, EF>;
     constexpr int V = G::VEC;
     constexpr bool BUF = RQ && !EF && !MASK;  // buffer addressing (see buf_load)
     const int lane = lane_id();
-    const size_t base = (BUF ? uniform64(tile) : tile) * (size_t)G::TILE;
     const size_t n = p.n;
     const size_t nbytes = (n + 1) / 2;
-
-    uint32_t cw[PMAX][G::U];  // code words (VEC nibbles each)
-    float sc[PMAX][G::U];
-    float e2[G::U][V];
-
-    // Issue every load of the tile first.
 #pragma unroll
     for (int q = 0; q < PMAX; ++q) {
         if (q < (int)p.P) {
@@ -216,6 +244,166 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
             }
         }
     }
+}
+
+// S = d_0 + d_1 + ..., ascending peer order, d = fl(k s) from the integer
+// nibble.  Peers are the outer loop so the runtime test q < P is one uniform
+// branch per peer, not a select per element.
+template <int PMAX, int U, int V>
+__device__ __forceinline__ void dr_sum_int(const DrParams& p, const uint32_t (&cw)[PMAX][U],
+                                           const float (&sc)[PMAX][U], float (&R)[U][V]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+            R[u][j] = nib(cw[0][u], j) * sc[0][u];
+#pragma unroll
+    for (int q = 1; q < PMAX; ++q) {
+        if (q < (int)p.P) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int j = 0; j < V; ++j)
+                    R[u][j] = R[u][j] + nib(cw[q][u], j) * sc[q][u];
+        }
+    }
+}
+
+// The same sum from k / 16 (v_cvt_off_f32_i4) times t = fl(16 s).  For
+// |s| < 2^124, t = 16 s exactly and every term equals fl(k s) bit for bit.
+// A larger, infinite or NaN s makes t infinite or NaN, so every term of that
+// block is infinite or NaN (a zero code gives 0 * inf = NaN) and so is every
+// sum of the block: the caller checks for that and redoes such a tile with
+// dr_sum_int.
+template <int PMAX, int U, int V>
+__device__ __forceinline__ void dr_sum_off(const DrParams& p, const uint32_t (&cw)[PMAX][U],
+                                           const float (&sc)[PMAX][U], float (&R)[U][V]) {
+    float f[V];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const float t = sc[0][u] * 16.0f;
+        nib16<V>(cw[0][u], f);
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+            R[u][j] = f[j] * t;
+    }
+#pragma unroll
+    for (int q = 1; q < PMAX; ++q) {
+        if (q < (int)p.P) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float t = sc[q][u] * 16.0f;
+                nib16<V>(cw[q][u], f);
+#pragma unroll
+                for (int j = 0; j < V; ++j)
+                    R[u][j] = R[u][j] + f[j] * t;
+            }
+        }
+    }
+}
+
+// dr_sum_int for one full tile, reloading the inputs one peer at a time in a
+// rolled loop: the rare redo path of the k / 16 decode, kept small so that
+// it adds no register pressure to the common path.
+template <int B, typename G>
+__device__ __forceinline__ void dr_sum_int_reload(const DrParams& p, size_t base,
+                                                  float (&R)[G::U][G::VEC]) {
+    constexpr int V = G::VEC;
+    const int lane = lane_id();
+#pragma nounroll
+    for (uint32_t q = 0; q < p.P; ++q) {
+        const uint8_t* codes = p.codes[q];
+        const float* scales = p.scales[q];
+#pragma unroll
+        for (int u = 0; u < G::U; ++u) {
+            const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
+            const uint32_t w = *(const code_word_t<V>*)(codes + i0 / 2);
+            const float s = scales[i0 / B];
+#pragma unroll
+            for (int j = 0; j < V; ++j)
+                R[u][j] = q == 0 ? nib(w, j) * s : R[u][j] + nib(w, j) * s;
+        }
+    }
+}
+
+// R = alpha R, skipped for alpha = 1 (multiplying by one is the identity).
+template <int U, int V>
+__device__ __forceinline__ void dr_alpha(const DrParams& p, float (&R)[U][V]) {
+    if (p.alpha != 1.0f) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < V; ++j)
+                R[u][j] = p.alpha * R[u][j];
+    }
+}
+
+// Requant input and block scales: c = R (+ the requant EF e2), in place;
+// elements past n are zeroed so that they do not enter the block max; then
+// the absmax of every block and its scale.
+template <int B, bool RQ, bool EF, bool MASK, typename G = DrGeomOf<B, RQ, EF>>
+__device__ __forceinline__ void rq_input(const DrParams& p, size_t base,
+                                         float (&c)[G::U][G::VEC],
+                                         const float (&e2)[G::U][G::VEC],
+                                         BlockScale (&bs)[G::SPB == 1 ? G::U : G::BPT]) {
+    constexpr int V = G::VEC;
+    if constexpr (EF) {
+#pragma unroll
+        for (int u = 0; u < G::U; ++u)
+#pragma unroll
+            for (int j = 0; j < V; ++j)
+                c[u][j] = c[u][j] + e2[u][j];
+    }
+    if constexpr (MASK) {
+        const int lane = lane_id();
+#pragma unroll
+        for (int u = 0; u < G::U; ++u) {
+            const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
+#pragma unroll
+            for (int j = 0; j < V; ++j)
+                if (i0 + j >= p.n)
+                    c[u][j] = 0.0f;
+        }
+    }
+    if constexpr (G::SPB == 1) {
+#pragma unroll
+        for (int u = 0; u < G::U; ++u) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int j = 0; j < V; ++j)
+                m = max(m, absbits(c[u][j]));
+            bs[u] = block_scale<7>(group_max<G::LPB>(m));
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < G::BPT; ++b) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int u = b * G::SPB; u < (b + 1) * G::SPB; ++u)
+#pragma unroll
+                for (int j = 0; j < V; ++j)
+                    m = max(m, absbits(c[u][j]));
+            bs[b] = block_scale<7>(group_max<kWave>(m));
+        }
+    }
+}
+
+template <int B, int PMAX, bool OUT, bool RQ, bool EF, bool MASK>
+__device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
+    constexpr bool RQEF = RQ && EF;  // requant with its EF buffer (p.rq_ef)
+    using G = DrGeomOf<B, RQ, EF>;
+    constexpr int V = G::VEC;
+    constexpr bool BUF = RQ && !EF && !MASK;  // buffer addressing (see buf_load)
+    const int lane = lane_id();
+    const size_t base = (BUF ? uniform64(tile) : tile) * (size_t)G::TILE;
+    const size_t n = p.n;
+
+    uint32_t cw[PMAX][G::U];  // code words (VEC nibbles each)
+    float sc[PMAX][G::U];
+    float e2[G::U][V];
+
+    // Issue every load of the tile first.
+    dr_load<B, PMAX, RQ, EF, MASK>(p, base, cw, sc);
     if constexpr (RQEF) {
 #pragma unroll
         for (int u = 0; u < G::U; ++u) {
@@ -235,32 +423,18 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
         }
     }
 
-    // Dequantize and reduce, ascending peer order.  Peers are the outer loop
-    // so the runtime test q < P is one uniform branch per peer, not a select
-    // per element; alpha = 1 is skipped (multiplying by one is the identity).
+    // Dequantize and reduce, then R = alpha S.  The requant-only flavours
+    // decode full tiles through k / 16 (dr_sum_off); a tile whose sums come
+    // out non-finite is redone from the integer decode inside the requant's
+    // rare branch below.  Every other flavour, and the ragged tail, takes the
+    // integer decode.
+    constexpr bool OFFDEC = ZQ_DR_DECODE_OFF && RQ && !OUT && !MASK;
     float R[G::U][V];
-#pragma unroll
-    for (int u = 0; u < G::U; ++u)
-#pragma unroll
-        for (int j = 0; j < V; ++j)
-            R[u][j] = nib(cw[0][u], j) * sc[0][u];
-#pragma unroll
-    for (int q = 1; q < PMAX; ++q) {
-        if (q < (int)p.P) {
-#pragma unroll
-            for (int u = 0; u < G::U; ++u)
-#pragma unroll
-                for (int j = 0; j < V; ++j)
-                    R[u][j] = R[u][j] + nib(cw[q][u], j) * sc[q][u];
-        }
-    }
-    if (p.alpha != 1.0f) {
-#pragma unroll
-        for (int u = 0; u < G::U; ++u)
-#pragma unroll
-            for (int j = 0; j < V; ++j)
-                R[u][j] = p.alpha * R[u][j];
-    }
+    if constexpr (OFFDEC)
+        dr_sum_off<PMAX, G::U, V>(p, cw, sc, R);
+    else
+        dr_sum_int<PMAX, G::U, V>(p, cw, sc, R);
+    dr_alpha<G::U, V>(p, R);
 
     if constexpr (OUT) {
 #pragma unroll
@@ -288,65 +462,8 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
     if constexpr (RQ) {
         // Compensated requant input, in place (R is not needed any more).
         float (&c)[G::U][V] = R;
-        if constexpr (RQEF) {
-#pragma unroll
-            for (int u = 0; u < G::U; ++u)
-#pragma unroll
-                for (int j = 0; j < V; ++j)
-                    c[u][j] = R[u][j] + e2[u][j];
-        }
-        // Beyond n the value must not enter the block max.
-        if constexpr (MASK) {
-#pragma unroll
-            for (int u = 0; u < G::U; ++u) {
-                const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
-#pragma unroll
-                for (int j = 0; j < V; ++j)
-                    if (i0 + j >= n)
-                        c[u][j] = 0.0f;
-            }
-        }
         BlockScale bs[G::SPB == 1 ? G::U : G::BPT];
-        if constexpr (G::SPB == 1) {
-#pragma unroll
-            for (int u = 0; u < G::U; ++u) {
-                uint32_t m = 0;
-#pragma unroll
-                for (int j = 0; j < V; ++j)
-                    m = max(m, absbits(c[u][j]));
-                bs[u] = block_scale<7>(group_max<G::LPB>(m));
-            }
-        } else {
-#pragma unroll
-            for (int b = 0; b < G::BPT; ++b) {
-                uint32_t m = 0;
-#pragma unroll
-                for (int u = b * G::SPB; u < (b + 1) * G::SPB; ++u)
-#pragma unroll
-                    for (int j = 0; j < V; ++j)
-                        m = max(m, absbits(c[u][j]));
-                bs[b] = block_scale<7>(group_max<kWave>(m));
-            }
-        }
-        if constexpr (G::SPB == 1) {
-            if (lane % G::LPB == 0) {
-#pragma unroll
-                for (int u = 0; u < G::U; ++u) {
-                    const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
-                    if (!MASK || i0 < n)
-                        p.rq_scales[i0 / B] = bs[u].s;
-                }
-            }
-        } else {
-            if (lane == 0) {
-#pragma unroll
-                for (int b = 0; b < G::BPT; ++b) {
-                    const size_t i0 = base + (size_t)b * B;
-                    if (!MASK || i0 < n)
-                        p.rq_scales[i0 / B] = bs[b].s;
-                }
-            }
-        }
+        rq_input<B, RQ, EF, MASK>(p, base, c, e2, bs);
         // Fast codes: rne(c * rcp(s)) by the 1.5 * 2^23 addition.  A tile
         // falls back to the IEEE quotient when an element is in the tie band
         // or a block scale is subnormal, infinite or NaN (uniform branch).
@@ -376,6 +493,25 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
                 }
             }
         } else {
+            if constexpr (OFFDEC) {
+                // Sums that are not all finite show up as a non-finite block
+                // scale: redo such a tile from the integer decode.
+                bool bad = false;
+#pragma unroll
+                for (int b = 0; b < (G::SPB == 1 ? G::U : G::BPT); ++b)
+                    bad |= !(bs[b].s <= 0x1.fffffep127f);
+                if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+                    dr_sum_int_reload<B, G>(p, base, R);
+                    dr_alpha<G::U, V>(p, R);
+                    rq_input<B, RQ, EF, MASK>(p, base, c, e2, bs);
+#pragma unroll
+                    for (int u = 0; u < G::U; ++u)
+#pragma unroll
+                        for (int j = 0; j < V; ++j)
+                            kf[u][j] = code_fast_rne<7>(c[u][j], bs[G::SPB == 1 ? u : u / G::SPB],
+                                                        bad);
+                }
+            }
 #pragma unroll
             for (int u = 0; u < G::U; ++u) {
                 const BlockScale& b = bs[G::SPB == 1 ? u : u / G::SPB];
@@ -386,6 +522,25 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
                     packed[u] |= ((uint32_t)k & 0xFu) << (4 * j);
                     if constexpr (RQEF)
                         e2[u][j] = ef_update(c[u][j], k, b.s, e2[u][j], p.rq_beta_e, p.rq_beta_r);
+                }
+            }
+        }
+        if constexpr (G::SPB == 1) {
+            if (lane % G::LPB == 0) {
+#pragma unroll
+                for (int u = 0; u < G::U; ++u) {
+                    const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
+                    if (!MASK || i0 < n)
+                        p.rq_scales[i0 / B] = bs[u].s;
+                }
+            }
+        } else {
+            if (lane == 0) {
+#pragma unroll
+                for (int b = 0; b < G::BPT; ++b) {
+                    const size_t i0 = base + (size_t)b * B;
+                    if (!MASK || i0 < n)
+                        p.rq_scales[i0 / B] = bs[b].s;
                 }
             }
         }
