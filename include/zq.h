@@ -109,9 +109,8 @@ zq_status zq_quantize_ef_int4(const void *g, zq_dtype g_dtype, float *ef, size_t
  * The n elements are n_part equal partitions of part_len = n / n_part
  * elements.  Partition p's codes and scales are written where partition
  * slot_of_part[p] would be in zq_quantize_ef_int4's output; g and ef keep
- * their natural order.  With intra GPUs per node and inter nodes (n_part =
- * intra * inter, rank r = node * intra + local), ZeRO++'s order is
- * slot_of_part[node * intra + local] = local * inter + node.
+ * their natural order.  ZeRO++'s order for intra GPUs per node and inter
+ * nodes (n_part = intra * inter) is what zq_zeropp_slots writes.
  *
  *   n_part        1 .. 256; part_len must be a multiple of block and at least
  *                 max(1024, block) (ZQ_ERR_SIZE otherwise).
@@ -262,6 +261,26 @@ typedef struct {
 
 zq_status zq_sr_accumulate_batched(const zq_sr_segment *segs, uint32_t n_seg, int zero_src,
                                    void *stream);
+
+/*
+ * zq_zeropp_slots -- ZeRO++'s partition order for zq_quantize_ef_int4_permuted
+ * ([ZeRO++] section 1.2: gradients are reduced inside the node first, then
+ * across nodes, and the slices are reordered before quantization so that
+ * both all-to-alls deliver each rank its own partition).  Host only.
+ *
+ * With `intra` GPUs per node and `inter` nodes, rank r = node * intra + local
+ * owns partition r.  The intra-node all-to-all sends chunk j of a GPU's
+ * quantized buffer (slots j * inter .. j * inter + inter - 1) to local rank
+ * j; after the intra-node reduce, sub-chunk i of the result goes to node i.
+ * Partition r must therefore sit in slot local * inter + node:
+ *   slot_of_part[node * intra + local] = local * inter + node.
+ *
+ *   slot_of_part  HOST array of intra * inter entries, written.
+ * Returns intra * inter, or 0 (writing nothing) when slot_of_part is NULL,
+ * intra or inter is 0, or intra * inter exceeds 256 (the most partitions
+ * zq_quantize_ef_int4_permuted takes).
+ */
+uint32_t zq_zeropp_slots(uint32_t intra, uint32_t inter, uint32_t *slot_of_part);
 
 /* Host-only helpers (no device work, usable without a GPU). */
 size_t zq_int4_code_bytes(size_t n);               /* ceil(n/2)                        */

@@ -38,13 +38,17 @@ def lib():
         L.orc_int4_decode.argtypes = [vp, sz]
         L.orc_int4_decode.restype = C.c_int32
         L.orc_quantize_ef_int4.argtypes = [vp, i32, vp, sz, u32, f32, f32, vp, vp]
-        L.orc_quantize_ef_int4.restype = None
+        L.orc_quantize_ef_int4.restype = i32
+        L.orc_quantize_ef_int4_permuted.argtypes = [vp, i32, vp, sz, u32, f32, f32, u32, vp, vp, vp]
+        L.orc_quantize_ef_int4_permuted.restype = i32
+        L.orc_zeropp_slots.argtypes = [u32, u32, vp]
+        L.orc_zeropp_slots.restype = i32
         L.orc_dequant_reduce.argtypes = [u32, vp, vp, sz, u32, f32, vp, vp, vp, vp, f32, f32, vp]
-        L.orc_dequant_reduce.restype = None
+        L.orc_dequant_reduce.restype = i32
         L.orc_quant_int8.argtypes = [vp, i32, sz, u32, vp, vp]
-        L.orc_quant_int8.restype = None
+        L.orc_quant_int8.restype = i32
         L.orc_dequant_int8.argtypes = [vp, vp, sz, u32, vp, i32]
-        L.orc_dequant_int8.restype = None
+        L.orc_dequant_int8.restype = i32
         L.orc_bf16_rne.argtypes = [f32]
         L.orc_bf16_rne.restype = C.c_uint16
         L.orc_philox4x32_10.argtypes = [vp, vp, vp]
@@ -54,13 +58,24 @@ def lib():
         L.orc_sr_round.argtypes = [f32, u32]
         L.orc_sr_round.restype = C.c_uint16
         L.orc_sr_accumulate.argtypes = [vp, vp, sz, u64, u64, i32]
-        L.orc_sr_accumulate.restype = None
+        L.orc_sr_accumulate.restype = i32
+        L.orc_sr_accumulate_segments.argtypes = [u32, vp, vp, vp, vp, vp, vp, vp, i32]
+        L.orc_sr_accumulate_segments.restype = i32
         L.orc_sr_r16_fill.argtypes = [u64, u64, sz, vp]
         L.orc_sr_r16_fill.restype = None
         L.orc_volume_bytes.argtypes = [u64, u32, u32, vp]
         L.orc_volume_bytes.restype = None
         _lib = L
     return _lib
+
+
+class OracleArgumentError(ValueError):
+    """The C oracle rejected its arguments (and wrote nothing)."""
+
+
+def _ok(rc: int, fn: str) -> None:
+    if rc != 0:
+        raise OracleArgumentError(f"{fn}: arguments rejected by the oracle ({rc})")
 
 
 def _ptr(a: np.ndarray | None):
@@ -119,8 +134,8 @@ def quantize_ef_int4(g: np.ndarray, ef: np.ndarray | None, block: int, beta_e: f
         assert ef.dtype == np.float32 and ef.size == n and ef.flags["C_CONTIGUOUS"]
     codes = np.full(int4_code_bytes(n), _POISON_U8, dtype=np.uint8)
     scales = np.full(num_blocks(n, block), np.nan, dtype=np.float32)
-    lib().orc_quantize_ef_int4(_ptr(g), is_bf16, _ptr(ef), n, block, beta_e, beta_r,
-                               _ptr(codes), _ptr(scales))
+    _ok(lib().orc_quantize_ef_int4(_ptr(g), is_bf16, _ptr(ef), n, block, beta_e, beta_r,
+                                   _ptr(codes), _ptr(scales)), "quantize_ef_int4")
     return codes, scales
 
 
@@ -144,8 +159,9 @@ def dequant_reduce(codes_list, scales_list, n_chunk: int, block: int, alpha: flo
     work = np.empty(max(n_chunk, 1), dtype=np.float32)
     if rq_ef is not None:
         assert requant and rq_ef.dtype == np.float32 and rq_ef.size == n_chunk
-    lib().orc_dequant_reduce(P, cptr, sptr, n_chunk, block, alpha, _ptr(out), _ptr(rq_codes),
-                             _ptr(rq_scales), _ptr(rq_ef), rq_beta_e, rq_beta_r, _ptr(work))
+    _ok(lib().orc_dequant_reduce(P, cptr, sptr, n_chunk, block, alpha, _ptr(out), _ptr(rq_codes),
+                                 _ptr(rq_scales), _ptr(rq_ef), rq_beta_e, rq_beta_r, _ptr(work)),
+        "dequant_reduce")
     return out, rq_codes, rq_scales
 
 
@@ -159,7 +175,8 @@ def quant_int8(w: np.ndarray, block: int):
         raise TypeError("w must be float32 or uint16 (bf16 bits)")
     codes = np.full(w.size, -86, dtype=np.int8)
     scales = np.full(num_blocks(w.size, block), np.nan, dtype=np.float32)
-    lib().orc_quant_int8(_ptr(w), is_bf16, w.size, block, _ptr(codes), _ptr(scales))
+    _ok(lib().orc_quant_int8(_ptr(w), is_bf16, w.size, block, _ptr(codes), _ptr(scales)),
+        "quant_int8")
     return codes, scales
 
 
@@ -169,8 +186,8 @@ def dequant_int8(codes: np.ndarray, scales: np.ndarray, block: int, out_bf16: bo
     codes = np.ascontiguousarray(codes, dtype=np.int8)
     scales = np.ascontiguousarray(scales, dtype=np.float32)
     out = np.zeros(codes.size, dtype=np.uint16 if out_bf16 else np.float32)
-    lib().orc_dequant_int8(_ptr(codes), _ptr(scales), codes.size, block, _ptr(out),
-                           1 if out_bf16 else 0)
+    _ok(lib().orc_dequant_int8(_ptr(codes), _ptr(scales), codes.size, block, _ptr(out),
+                               1 if out_bf16 else 0), "dequant_int8")
     return out
 
 
@@ -209,8 +226,8 @@ def sr_accumulate(dst: np.ndarray, src: np.ndarray, seed: int, counter_base: int
     when zero_src).  Both uint16 bf16 bit arrays of equal size."""
     assert dst.dtype == np.uint16 and src.dtype == np.uint16 and dst.size == src.size
     assert dst.flags["C_CONTIGUOUS"] and src.flags["C_CONTIGUOUS"]
-    lib().orc_sr_accumulate(_ptr(dst), _ptr(src), dst.size, seed, counter_base,
-                            1 if zero_src else 0)
+    _ok(lib().orc_sr_accumulate(_ptr(dst), _ptr(src), dst.size, seed, counter_base,
+                                1 if zero_src else 0), "sr_accumulate")
 
 
 def volume_bytes(M: int, block_w: int, block_g: int):
@@ -223,35 +240,58 @@ def volume_bytes(M: int, block_w: int, block_g: int):
 
 def sr_accumulate_segments(segments, zero_src: bool):
     """llm.c's per-tensor ZeRO-2 loop ("Zero 2 #593", review of
-    llmc/zero.cuh): for each segment (dst, src, n, src_offset, seed,
-    counter_base), dst[0:n] += src[src_offset:src_offset+n] with stochastic
-    rounding, then -- with zero_src -- the whole src buffer is cleared (the
-    memset the review suggests folding into the add).  In place on the given
-    uint16 (bf16 bit) arrays."""
-    for dst, src, n, off, seed, cb in segments:
-        if n:
-            sl = src[off:off + n]
-            assert sl.flags["C_CONTIGUOUS"]
-            sr_accumulate(dst[:n], sl, seed, cb, zero_src=False)
-        if zero_src:
-            src[:] = 0
+    llmc/zero.cuh), done by the C oracle: for each segment (dst, src, n,
+    src_offset, seed, counter_base), dst[0:n] += src[src_offset:src_offset+n]
+    with stochastic rounding, then -- with zero_src -- the whole src buffer
+    is cleared (the memset the review suggests folding into the add).  In
+    place on the given contiguous uint16 (bf16 bit) arrays."""
+    segs = list(segments)
+    m = len(segs)
+    for dst, src, n, off, _, _ in segs:
+        assert dst.dtype == np.uint16 and src.dtype == np.uint16
+        assert dst.flags["C_CONTIGUOUS"] and src.flags["C_CONTIGUOUS"] and dst.size >= n
+    ptrs = lambda arrs: (C.c_void_p * max(m, 1))(*[a.ctypes.data for a in arrs])
+    u64s = lambda vals: np.array(list(vals) or [0], dtype=np.uint64)
+    n = u64s(s[2] for s in segs)
+    off = u64s(s[3] for s in segs)
+    ln = u64s(s[1].size for s in segs)
+    seed = u64s(s[4] for s in segs)
+    cb = u64s(s[5] for s in segs)
+    _ok(lib().orc_sr_accumulate_segments(m, ptrs([s[0] for s in segs]), ptrs([s[1] for s in segs]),
+                                         _ptr(n), _ptr(off), _ptr(ln), _ptr(seed), _ptr(cb),
+                                         1 if zero_src else 0), "sr_accumulate_segments")
+
+
+def zeropp_slots(intra: int, inter: int) -> list[int]:
+    """ZeRO++'s partition order for `inter` nodes of `intra` GPUs
+    ("ZeROPlusPlus.md" notes, section 1.2: reduce inside the node, then
+    across nodes): slot_of_part[r] for rank r = node * intra + local."""
+    out = np.zeros(max(intra * inter, 1), dtype=np.uint32)
+    _ok(lib().orc_zeropp_slots(intra, inter, _ptr(out)), "zeropp_slots")
+    return [int(v) for v in out[:intra * inter]]
 
 
 def quantize_ef_int4_permuted(g, ef, block: int, beta_e: float, beta_r: float, slot_of_part):
     """The EF int4 quantizer with its outputs in permuted partition order
     ("ZeROPlusPlus.md" notes, section 1.2: hierarchical gradient reduction,
-    inside the node first, then across nodes): the plain quantizer, then the
-    codes and scales of partition p placed where partition slot_of_part[p]
-    would be.  Partitions are equal and whole blocks long."""
-    n = np.asarray(g).size
-    n_part = len(slot_of_part)
-    part = n // n_part
-    assert part * n_part == n and part % block == 0 and part % 2 == 0
-    codes, scales = quantize_ef_int4(g, ef, block, beta_e, beta_r)
-    c_out = np.empty_like(codes)
-    s_out = np.empty_like(scales)
-    cb, sb = part // 2, part // block
-    for p, slot in enumerate(slot_of_part):
-        c_out[slot * cb:(slot + 1) * cb] = codes[p * cb:(p + 1) * cb]
-        s_out[slot * sb:(slot + 1) * sb] = scales[p * sb:(p + 1) * sb]
-    return c_out, s_out
+    inside the node first, then across nodes), done by the C oracle: the
+    codes and scales of partition p are stored where partition
+    slot_of_part[p] would be.  Partitions are equal and whole blocks long."""
+    _check_block(block)
+    g = np.ascontiguousarray(g)
+    if g.dtype == np.uint16:
+        is_bf16 = 1
+    elif g.dtype == np.float32:
+        is_bf16 = 0
+    else:
+        raise TypeError("g must be float32 or uint16 (bf16 bits)")
+    n = g.size
+    if ef is not None:
+        assert ef.dtype == np.float32 and ef.size == n and ef.flags["C_CONTIGUOUS"]
+    slots = np.ascontiguousarray(slot_of_part, dtype=np.uint32)
+    codes = np.full(int4_code_bytes(n), _POISON_U8, dtype=np.uint8)
+    scales = np.full(num_blocks(n, block), np.nan, dtype=np.float32)
+    _ok(lib().orc_quantize_ef_int4_permuted(_ptr(g), is_bf16, _ptr(ef), n, block, beta_e, beta_r,
+                                            slots.size, _ptr(slots), _ptr(codes), _ptr(scales)),
+        "quantize_ef_int4_permuted")
+    return codes, scales

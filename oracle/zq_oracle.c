@@ -26,9 +26,15 @@
  * compiler neither fuses a*b+c into one rounding nor reorders anything.
  *
  * Parity status of each function (pins live in the CPU test suite):
- *   orc_quant_block, orc_quantize_ef_int4, orc_dequant_reduce,
- *   orc_quant_int8, orc_dequant_int8, orc_bf16_rne, orc_sr_round,
- *   orc_philox4x32_10, orc_sr_accumulate, orc_volume_bytes: pinned.
+ *   orc_quant_block, orc_quantize_ef_int4, orc_quantize_ef_int4_permuted,
+ *   orc_zeropp_slots, orc_dequant_reduce, orc_quant_int8, orc_dequant_int8,
+ *   orc_bf16_rne, orc_sr_round, orc_philox4x32_10, orc_sr_accumulate,
+ *   orc_sr_accumulate_segments, orc_volume_bytes: pinned.
+ *
+ * Every entry point that takes buffers checks its arguments first and
+ * returns ORC_EINVAL (writing nothing) on NULL outputs, a block size the
+ * fixed per-block work arrays cannot hold (block must be even and in
+ * [2, 4096]), or inconsistent sizes; 0 means done.
  *   Agreement with DeepSpeed's or llm.c's own numerics: parity unpinned
  *   (the pages carry no code or outputs of theirs).
  */
@@ -36,6 +42,10 @@
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
+
+#define ORC_EINVAL (-1)
+
+static int bad_block(uint32_t block) { return block < 2 || block > 4096 || (block & 1u); }
 
 /* ---------------------------------------------------------------- bf16 -- */
 
@@ -94,10 +104,11 @@ void orc_quant_block(const float *x, size_t m, int qmax, int32_t *k, float *s_ou
         }
         float q = x[i] / s;
         float r = rintf(q); /* default rounding mode: nearest, ties to even */
-        if (r > (float)qmax)
-            r = (float)qmax;
-        if (r < -(float)qmax)
-            r = -(float)qmax;
+        /* clamp to [-qmax, qmax] with IEEE maxNum / minNum: for any number
+         * this is the plain clamp; a NaN quotient, which only non-finite
+         * inputs produce (outside the contract), gives -qmax */
+        r = fmaxf(r, -(float)qmax);
+        r = fminf(r, (float)qmax);
         k[i] = (int32_t)r;
     }
     *s_out = s;
@@ -137,9 +148,11 @@ int32_t orc_int4_decode(const uint8_t *codes, size_t i) { return get_nibble(code
  * codes: ceil(n/2) bytes, scales: ceil(n/block) floats, ef: n floats or NULL.
  * block must be even and at most 4096.  The last block may be partial; its
  * scale uses only its own elements. */
-void orc_quantize_ef_int4(const void *g, int g_is_bf16, float *ef, size_t n, uint32_t block,
-                          float beta_e, float beta_r, uint8_t *codes, float *scales)
+int orc_quantize_ef_int4(const void *g, int g_is_bf16, float *ef, size_t n, uint32_t block,
+                         float beta_e, float beta_r, uint8_t *codes, float *scales)
 {
+    if (bad_block(block) || (n > 0 && (!g || !codes || !scales)))
+        return ORC_EINVAL;
     float c[4096];
     int32_t k[4096];
     size_t nb = (n + block - 1) / block;
@@ -168,6 +181,63 @@ void orc_quantize_ef_int4(const void *g, int g_is_bf16, float *ef, size_t n, uin
         if (m & 1u) /* odd element count: the unused high nibble is zero */
             codes[(lo + m) / 2] &= 0x0Fu;
     }
+    return 0;
+}
+
+/* ----------------------------- hierarchical partition order (ZeRO++) -- */
+
+/* ZeRO++ reduces gradients hierarchically, inside the node first and then
+ * across nodes ([ZeRO++] section 1.2).  With `intra` GPUs per node and
+ * `inter` nodes, rank r = node * intra + local owns partition r.  The
+ * intra-node all-to-all sends chunk j of each GPU's buffer -- slots
+ * j * inter .. j * inter + inter - 1 -- to local rank j; after the intra-node
+ * reduction the inter-node all-to-all sends sub-chunk i of that result to
+ * node i.  Partition r therefore has to sit in slot local * inter + node for
+ * the two exchanges to bring it to rank r.  slot_of_part gets intra * inter
+ * entries. */
+int orc_zeropp_slots(uint32_t intra, uint32_t inter, uint32_t *slot_of_part)
+{
+    if (intra < 1 || inter < 1 || !slot_of_part)
+        return ORC_EINVAL;
+    for (uint32_t node = 0; node < inter; node++)
+        for (uint32_t local = 0; local < intra; local++)
+            slot_of_part[node * intra + local] = local * inter + node;
+    return 0;
+}
+
+/* The EF int4 quantizer above with its outputs in a permuted partition
+ * order.  The n elements form n_part equal partitions of whole blocks;
+ * partition p is quantized exactly as orc_quantize_ef_int4 quantizes those
+ * elements within the whole buffer (its blocks are the same blocks), and
+ * its codes and scales are stored where partition slot_of_part[p] lies in
+ * that function's layout.  g and ef keep their natural order. */
+int orc_quantize_ef_int4_permuted(const void *g, int g_is_bf16, float *ef, size_t n,
+                                  uint32_t block, float beta_e, float beta_r, uint32_t n_part,
+                                  const uint32_t *slot_of_part, uint8_t *codes, float *scales)
+{
+    if (bad_block(block) || n_part < 1 || !slot_of_part || !g || !codes || !scales)
+        return ORC_EINVAL;
+    size_t part = n / n_part;
+    if (part * n_part != n || part % block != 0)
+        return ORC_EINVAL;
+    for (uint32_t p = 0; p < n_part; p++) { /* a permutation of 0 .. n_part-1 */
+        if (slot_of_part[p] >= n_part)
+            return ORC_EINVAL;
+        for (uint32_t q = 0; q < p; q++)
+            if (slot_of_part[q] == slot_of_part[p])
+                return ORC_EINVAL;
+    }
+    for (uint32_t p = 0; p < n_part; p++) {
+        size_t from = p * part;
+        size_t to = slot_of_part[p] * part;
+        const void *gp = g_is_bf16 ? (const void *)((const uint16_t *)g + from)
+                                   : (const void *)((const float *)g + from);
+        int rc = orc_quantize_ef_int4(gp, g_is_bf16, ef ? ef + from : NULL, part, block, beta_e,
+                                      beta_r, codes + to / 2, scales + to / block);
+        if (rc)
+            return rc;
+    }
+    return 0;
 }
 
 /* --------------------------------- dequantize + full-precision reduce -- */
@@ -180,11 +250,17 @@ void orc_quantize_ef_int4(const void *g, int g_is_bf16, float *ef, size_t n, uin
  * R is quantized again for the next level of the hierarchy (reduce inside
  * the node, then across nodes): the EF int4 quantizer above with input R,
  * optional EF buffer rq_ef and coefficients (rq_beta_e, rq_beta_r). */
-void orc_dequant_reduce(uint32_t P, const uint8_t *const *codes, const float *const *scales,
-                        size_t n_chunk, uint32_t block, float alpha, float *out,
-                        uint8_t *rq_codes, float *rq_scales, float *rq_ef,
-                        float rq_beta_e, float rq_beta_r, float *work /* n_chunk floats */)
+int orc_dequant_reduce(uint32_t P, const uint8_t *const *codes, const float *const *scales,
+                       size_t n_chunk, uint32_t block, float alpha, float *out,
+                       uint8_t *rq_codes, float *rq_scales, float *rq_ef,
+                       float rq_beta_e, float rq_beta_r, float *work /* n_chunk floats */)
 {
+    if (bad_block(block) || P < 1 || !codes || !scales || (!out && !rq_codes) ||
+        (rq_codes && !rq_scales) || (rq_ef && !rq_codes) || (n_chunk > 0 && !work))
+        return ORC_EINVAL;
+    for (uint32_t p = 0; p < P; p++)
+        if (n_chunk > 0 && (!codes[p] || !scales[p]))
+            return ORC_EINVAL;
     for (size_t i = 0; i < n_chunk; i++) {
         size_t b = i / block;
         float S = (float)get_nibble(codes[0], i) * scales[0][b];
@@ -198,7 +274,9 @@ void orc_dequant_reduce(uint32_t P, const uint8_t *const *codes, const float *co
             out[i] = R;
     }
     if (rq_codes)
-        orc_quantize_ef_int4(work, 0, rq_ef, n_chunk, block, rq_beta_e, rq_beta_r, rq_codes, rq_scales);
+        return orc_quantize_ef_int4(work, 0, rq_ef, n_chunk, block, rq_beta_e, rq_beta_r, rq_codes,
+                                    rq_scales);
+    return 0;
 }
 
 /* ------------------------------------------------ qwZ int8 weights -- */
@@ -206,9 +284,11 @@ void orc_dequant_reduce(uint32_t P, const uint8_t *const *codes, const float *co
 /* Block int8 weight quantization before the forward all-gather ([ZeRO++]
  * section 1.2, qwZ): the block quantizer with qmax = 127, one fp32 scale per
  * block, codes stored as int8. */
-void orc_quant_int8(const void *w, int w_is_bf16, size_t n, uint32_t block, int8_t *codes,
-                    float *scales)
+int orc_quant_int8(const void *w, int w_is_bf16, size_t n, uint32_t block, int8_t *codes,
+                   float *scales)
 {
+    if (bad_block(block) || (n > 0 && (!w || !codes || !scales)))
+        return ORC_EINVAL;
     float x[4096];
     int32_t k[4096];
     size_t nb = (n + block - 1) / block;
@@ -221,13 +301,16 @@ void orc_quant_int8(const void *w, int w_is_bf16, size_t n, uint32_t block, int8
         for (size_t j = 0; j < m; j++)
             codes[lo + j] = (int8_t)k[j];
     }
+    return 0;
 }
 
 /* Dequantize after the all-gather: w' = fl(k * s), stored as fp32 or as
  * bf16 rounded to nearest even from that fp32 value. */
-void orc_dequant_int8(const int8_t *codes, const float *scales, size_t n, uint32_t block,
-                      void *out, int out_is_bf16)
+int orc_dequant_int8(const int8_t *codes, const float *scales, size_t n, uint32_t block,
+                     void *out, int out_is_bf16)
 {
+    if (block < 1 || (n > 0 && (!codes || !scales || !out)))
+        return ORC_EINVAL;
     for (size_t i = 0; i < n; i++) {
         float v = (float)codes[i] * scales[i / block];
         if (out_is_bf16)
@@ -235,6 +318,7 @@ void orc_dequant_int8(const int8_t *codes, const float *scales, size_t n, uint32
         else
             ((float *)out)[i] = v;
     }
+    return 0;
 }
 
 /* ------------------------------------------------------- Philox4x32 -- */
@@ -314,15 +398,46 @@ uint16_t orc_sr_round(float x, uint32_t r16)
  * that of global index counter_base + i.  With zero_src, the source element
  * is cleared after it is read (the pages' suggestion to fold the zeroing of
  * the reduced buffer into the add). */
-void orc_sr_accumulate(uint16_t *dst, uint16_t *src, size_t n, uint64_t seed,
-                       uint64_t counter_base, int zero_src)
+int orc_sr_accumulate(uint16_t *dst, uint16_t *src, size_t n, uint64_t seed,
+                      uint64_t counter_base, int zero_src)
 {
+    if (n > 0 && (!dst || !src))
+        return ORC_EINVAL;
     for (size_t i = 0; i < n; i++) {
         float x = bf16_to_f32(dst[i]) + bf16_to_f32(src[i]);
         dst[i] = orc_sr_round(x, orc_sr_r16(seed, counter_base + i));
         if (zero_src)
             src[i] = 0;
     }
+    return 0;
+}
+
+/* llm.c's per-tensor ZeRO-2 gradient accumulation ([llm.c] review of
+ * llmc/zero.cuh): for tensor i in order, its shard dst[i][0, n[i])
+ * accumulates the slice src[i][off[i], off[i] + n[i]) of the tensor's
+ * reduced buffer with the stochastic-rounding add above (seed[i], counter
+ * base cbase[i]); then, with zero_src, the whole reduced buffer
+ * src[i][0, len[i]) is set to zero -- the memset the reviewers suggest
+ * folding into the add. */
+int orc_sr_accumulate_segments(uint32_t n_seg, uint16_t *const *dst, uint16_t *const *src,
+                               const uint64_t *n, const uint64_t *off, const uint64_t *len,
+                               const uint64_t *seed, const uint64_t *cbase, int zero_src)
+{
+    if (n_seg > 0 && (!dst || !src || !n || !off || !len || !seed || !cbase))
+        return ORC_EINVAL;
+    for (uint32_t i = 0; i < n_seg; i++) {
+        if (off[i] > len[i] || n[i] > len[i] - off[i])
+            return ORC_EINVAL;
+        if ((n[i] > 0 && !dst[i]) || ((n[i] > 0 || (zero_src && len[i] > 0)) && !src[i]))
+            return ORC_EINVAL;
+    }
+    for (uint32_t i = 0; i < n_seg; i++) {
+        if (n[i] > 0)
+            orc_sr_accumulate(dst[i], src[i] + off[i], n[i], seed[i], cbase[i], 0);
+        if (zero_src && len[i] > 0)
+            memset(src[i], 0, len[i] * sizeof(uint16_t));
+    }
+    return 0;
 }
 
 /* ------------------------------------------- communication volume -- */

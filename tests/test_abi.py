@@ -20,7 +20,7 @@ def test_exports_every_declared_symbol():
                           "zq_quantize_ef_int4_batched",
                           "zq_dequant_reduce", "zq_quant_int8",
                           "zq_dequant_int8", "zq_sr_accumulate", "zq_sr_accumulate_batched",
-                          "zq_int4_code_bytes",
+                          "zq_int4_code_bytes", "zq_zeropp_slots",
                           "zq_num_blocks", "zq_status_str", "zq_abi_version"}
     for name in names:
         assert hasattr(L, name), name
@@ -177,7 +177,28 @@ def test_permuted_quantize_validation():
     assert call(n=0, g=None) == zq.ZQ_OK
     assert call(codes=FAKE + 0x1000002) == zq.ZQ_ERR_ALIGN
     assert call(codes=FAKE + 0x100) == zq.ZQ_ERR_ALIAS
-    assert zq.zeropp_slots(4, 2) == [0, 2, 4, 6, 1, 3, 5, 7]
+
+
+def test_zeropp_slots_through_the_c_abi(golden_dir):
+    """zq_zeropp_slots against the hand-worked tables of the pages' two-level
+    order, through the raw C ABI, and the binding passing it through."""
+    import json
+    import os
+    with open(os.path.join(golden_dir, "zeropp_order_worked.json")) as f:
+        G = json.load(f)["slots"]
+    for (intra, inter), key in (((4, 2), "intra4_inter2"), ((8, 4), "intra8_inter4"),
+                                ((1, 3), "intra1_inter3"), ((3, 1), "intra3_inter1")):
+        out = (C.c_uint32 * (intra * inter))(*([0xDEAD] * (intra * inter)))
+        assert L.zq_zeropp_slots(intra, inter, out) == intra * inter
+        assert list(out) == G[key]
+        assert zq.zeropp_slots(intra, inter) == G[key]
+    out = (C.c_uint32 * 4)(7, 7, 7, 7)
+    for intra, inter in ((0, 4), (4, 0), (16, 17)):
+        assert L.zq_zeropp_slots(intra, inter, out) == 0
+    assert L.zq_zeropp_slots(2, 2, None) == 0
+    assert list(out) == [7, 7, 7, 7]
+    with pytest.raises(ValueError):
+        zq.zeropp_slots(0, 2)
 
 
 def test_efq_batched_validation():

@@ -476,8 +476,10 @@ def test_hierarchical_qgz_delivers_each_rank_its_partition():
     chunk l of its node peers (8-way... here 4-way reduce + requant), the
     inter-node all-to-all hands node n sub-chunk n of the same local rank on
     every node (2-way reduce, alpha 1/8).  Rank r = node*4 + local must end
-    with the average of partition r of all 8 gradients -- bit-exact against
-    the oracle running the same exchanges, and close to the exact mean."""
+    with the average of partition r of all 8 gradients: bit-exact against
+    the oracle running the same exchanges, and bit-exact against the
+    natural-order quantizer with the same two-level reduction of partition r
+    alone (the meaning of the order, as pinned on the CPU)."""
     from weight_communication_zero_amd import zeropp_slots
     intra, inter, B = 4, 2, 128
     R = intra * inter
@@ -493,6 +495,7 @@ def test_hierarchical_qgz_delivers_each_rank_its_partition():
         Z().zq_quantize_ef_int4_permuted(to_gpu(grads[r]), None, B, 0.0, 1.0, c, s, slots)
         c_o, s_o = O.quantize_ef_int4_permuted(grads[r], None, B, 0.0, 1.0, slots)
         cg.append(c), sg.append(s), co.append(c_o), so.append(s_o)
+    nat = [O.quantize_ef_int4(grads[r], None, B, 0.0, 1.0) for r in range(R)]
     chunk = M // intra  # level-1 chunk: slots [l*inter, (l+1)*inter)
     l1_g, l1_o = {}, {}
     for node in range(inter):
@@ -522,6 +525,18 @@ def test_hierarchical_qgz_delivers_each_rank_its_partition():
             torch.cuda.synchronize()
             got = to_host(out)
             assert_bits_equal(got, out_o, f"rank {r} final shard")
+            # what partition r must be: the natural-order quantizer and the
+            # same two-level reduction over partition r alone
+            sub = []
+            for nd in range(inter):
+                recv = [(nat[nd * intra + q][0][r * part // 2:(r + 1) * part // 2],
+                         nat[nd * intra + q][1][r * part // B:(r + 1) * part // B])
+                        for q in range(intra)]
+                _, rc_n, rs_n = O.dequant_reduce([a for a, _ in recv], [b for _, b in recv], part,
+                                                 B, 1.0, want_out=False, requant=True)
+                sub.append((rc_n, rs_n))
+            want, _, _ = O.dequant_reduce([a for a, _ in sub], [b for _, b in sub], part, B, 1.0 / R)
+            assert_bits_equal(got, want, f"rank {r} holds partition {r}")
             exact = np.mean([g[r * part:(r + 1) * part].astype(np.float64) for g in grads], axis=0)
             err = np.abs(got - exact)
             assert np.corrcoef(got, exact)[0, 1] > 0.95, f"rank {r} did not receive partition {r}"

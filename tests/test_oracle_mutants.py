@@ -34,7 +34,8 @@ MUTANTS = [
     ("scale by reciprocal multiply", "float s = a / (float)qmax;", "float s = a * (1.0f / (float)qmax);"),
     ("signed maximum instead of absmax", "float v = fabsf(x[i]);", "float v = x[i];"),
     ("ties away from zero", "float r = rintf(q); /*", "float r = roundf(q); /*"),
-    ("upper clamp dropped", "if (r > (float)qmax)\n            r = (float)qmax;", ""),
+    ("upper clamp dropped", "r = fminf(r, (float)qmax);", ""),
+    ("lower clamp dropped", "r = fmaxf(r, -(float)qmax);", ""),
     ("nibble order swapped", "if ((i & 1u) == 0)\n        codes[i / 2]", "if ((i & 1u) == 1)\n        codes[i / 2]"),
     ("nibble sign extension off by one", "(int32_t)nib - 16", "(int32_t)nib - 15"),
     ("odd tail's high nibble not cleared", "codes[(lo + m) / 2] &= 0x0Fu;", ";"),
@@ -59,6 +60,23 @@ MUTANTS = [
     ("volume counts int4 as a byte", "uint64_t qgz = (M + 1) / 2 +", "uint64_t qgz = M +"),
     ("volume drops the weight scales", "uint64_t qwz = M + 4u * ((M + block_w - 1) / block_w);",
      "uint64_t qwz = M;"),
+    ("ZeRO++ slots: identity order", "slot_of_part[node * intra + local] = local * inter + node;",
+     "slot_of_part[node * intra + local] = node * intra + local;"),
+    ("ZeRO++ slots: inverse map", "slot_of_part[node * intra + local] = local * inter + node;",
+     "slot_of_part[local * inter + node] = node * intra + local;"),
+    ("permuted quantize: inverse slot map",
+     "size_t from = p * part;\n        size_t to = slot_of_part[p] * part;",
+     "size_t from = slot_of_part[p] * part;\n        size_t to = p * part;"),
+    ("permuted quantize: EF buffer permuted too", "ef ? ef + from : NULL", "ef ? ef + to : NULL"),
+    ("segments: only the slice read is cleared", "memset(src[i], 0, len[i] * sizeof(uint16_t));",
+     "memset(src[i] + off[i], 0, n[i] * sizeof(uint16_t));"),
+    ("segments: cleared before the add",
+     "        if (n[i] > 0)\n            orc_sr_accumulate(dst[i], src[i] + off[i], n[i], seed[i], cbase[i], 0);\n"
+     "        if (zero_src && len[i] > 0)\n            memset(src[i], 0, len[i] * sizeof(uint16_t));",
+     "        if (zero_src && len[i] > 0)\n            memset(src[i], 0, len[i] * sizeof(uint16_t));\n"
+     "        if (n[i] > 0)\n            orc_sr_accumulate(dst[i], src[i] + off[i], n[i], seed[i], cbase[i], 0);"),
+    ("segments: counter base taken from the offset", "seed[i], cbase[i], 0);", "seed[i], cbase[i] + off[i], 0);"),
+    ("segments: one seed for all", "n[i], seed[i], cbase[i], 0);", "n[i], seed[0], cbase[i], 0);"),
 ]
 
 

@@ -594,3 +594,168 @@ def test_volume_closed_form_against_pages(golden_dir):
     units = zpp / (2 * M)
     assert abs(units - (0.75 + 2 / 2048 + 2 / 128)) < 1e-12
     assert 3.9 < zero3 / zpp < 3.92
+
+
+# ------------------------------------------- ZeRO++ hierarchical order --
+
+def test_zeropp_slots_worked(golden_dir):
+    G = load(golden_dir, "zeropp_order_worked.json")["slots"]
+    assert O.zeropp_slots(4, 2) == G["intra4_inter2"]
+    assert O.zeropp_slots(8, 4) == G["intra8_inter4"]
+    assert O.zeropp_slots(1, 3) == G["intra1_inter3"]
+    assert O.zeropp_slots(3, 1) == G["intra3_inter1"]
+
+
+def test_quantize_permuted_worked(golden_dir):
+    G = load(golden_dir, "zeropp_order_worked.json")["quantize_permuted"]
+    g = np.array(G["g"], np.float32)
+    ef = np.zeros(g.size, np.float32)
+    codes, scales = O.quantize_ef_int4_permuted(g, ef, G["block"], G["beta_e"], G["beta_r"],
+                                                G["slot_of_part"])
+    assert codes.tolist() == hexbytes(G["codes"]).tolist()
+    assert scales.tolist() == G["scales"]
+    assert ef.tolist() == G["ef_after"]
+
+
+def test_quantize_permuted_identity_order_is_the_plain_quantizer():
+    n, B = 4096, 64
+    g = (RNG.standard_normal(n) * 1e-3).astype(np.float32)
+    e1 = (RNG.standard_normal(n) * 1e-4).astype(np.float32)
+    e2 = e1.copy()
+    c1, s1 = O.quantize_ef_int4_permuted(g, e1, B, 0.9, 1.0, list(range(8)))
+    c2, s2 = O.quantize_ef_int4(g, e2, B, 0.9, 1.0)
+    assert (c1 == c2).all() and (s1.view(np.uint32) == s2.view(np.uint32)).all()
+    assert (e1.view(np.uint32) == e2.view(np.uint32)).all()
+    with pytest.raises(O.OracleArgumentError):  # not a permutation
+        O.quantize_ef_int4_permuted(g, None, B, 0.9, 1.0, [0, 1, 2, 3, 4, 5, 6, 6])
+    with pytest.raises(O.OracleArgumentError):  # partitions not whole blocks
+        O.quantize_ef_int4_permuted(g[:4096 - 8 * 16], None, B, 0.9, 1.0, list(range(8)))
+
+
+def _chunk(codes, scales, lo, m, B):
+    """Codes and scales of elements [lo, lo + m) of a quantized buffer."""
+    return codes[lo // 2:(lo + m) // 2], scales[lo // B:(lo + m) // B]
+
+
+@pytest.mark.parametrize("intra,inter", [(4, 2), (2, 3)])
+def test_two_level_exchange_delivers_each_rank_its_partition(intra, inter):
+    """Simulate hierarchical qgZ on the CPU with the oracle: every rank
+    quantizes its gradient into ZeRO++'s order; the intra-node all-to-all
+    sends chunk j of a buffer to local rank j, which reduces the chunks of
+    its node and requantizes; the inter-node all-to-all sends sub-chunk i of
+    that to node i, which reduces over nodes.  Rank r must end with exactly
+    what the natural-order quantizer and the same two-level reduction give
+    for partition r -- the meaning of the order, not its formula."""
+    R, B, part = intra * inter, 32, 256
+    n = R * part
+    rng = np.random.default_rng(intra * 10 + inter)
+    grads = [(rng.standard_normal(n) * 1e-3).astype(np.float32) for _ in range(R)]
+    ef0 = [(rng.standard_normal(n) * 1e-5).astype(np.float32) for _ in range(R)]
+    slots = O.zeropp_slots(intra, inter)
+    rank = lambda node, local: node * intra + local
+    # permuted path, as the exchanges would run it
+    ef_p = [e.copy() for e in ef0]
+    q = [O.quantize_ef_int4_permuted(grads[r], ef_p[r], B, 0.9, 1.0, slots) for r in range(R)]
+    chunk = inter * part  # elements per intra-node chunk
+    lvl1 = {}
+    for node in range(inter):
+        for j in range(intra):
+            recv = [_chunk(*q[rank(node, i)], j * chunk, chunk, B) for i in range(intra)]
+            _, rc, rs = O.dequant_reduce([c for c, _ in recv], [s for _, s in recv], chunk, B, 1.0,
+                                         want_out=False, requant=True)
+            lvl1[node, j] = (rc, rs)
+    final = {}
+    for node in range(inter):
+        for j in range(intra):
+            recv = [_chunk(*lvl1[other, j], node * part, part, B) for other in range(inter)]
+            out, _, _ = O.dequant_reduce([c for c, _ in recv], [s for _, s in recv], part, B,
+                                         1.0 / R)
+            final[rank(node, j)] = out
+    # natural order: partition r reduced over the ranks of each node, then over nodes
+    ef_n = [e.copy() for e in ef0]
+    nat = [O.quantize_ef_int4(grads[r], ef_n[r], B, 0.9, 1.0) for r in range(R)]
+    for node in range(inter):
+        for j in range(intra):
+            r = rank(node, j)
+            sub = []
+            for other in range(inter):
+                recv = [_chunk(*nat[rank(other, i)], r * part, part, B) for i in range(intra)]
+                _, rc, rs = O.dequant_reduce([c for c, _ in recv], [s for _, s in recv], part, B,
+                                             1.0, want_out=False, requant=True)
+                sub.append((rc, rs))
+            out, _, _ = O.dequant_reduce([c for c, _ in sub], [s for _, s in sub], part, B, 1.0 / R)
+            assert (final[r].view(np.uint32) == out.view(np.uint32)).all(), (intra, inter, r)
+    for r in range(R):  # the error feedback stays in natural order
+        assert (ef_p[r].view(np.uint32) == ef_n[r].view(np.uint32)).all()
+
+
+# -------------------------------------- per-tensor SR loop (llm.c ZeRO-2) --
+
+def _seg_fixture(golden_dir):
+    G = load(golden_dir, "sr_segments_worked.json")
+    h = lambda lst: np.array([int(x, 16) for x in lst], np.uint16)
+    segs = []
+    for c in G["segments"]:
+        segs.append((h(c["dst"]), h(c["src"]), c["n"], c["src_offset"], c["seed"],
+                     c["counter_base"]))
+    return G, segs
+
+
+@pytest.mark.parametrize("zero_src", [False, True])
+def test_sr_segments_worked(golden_dir, zero_src):
+    G, segs = _seg_fixture(golden_dir)
+    src_before = [s[1].copy() for s in segs]
+    O.sr_accumulate_segments(segs, zero_src=zero_src)
+    thr = int(G["round_up_threshold"], 16)
+    for c, (dst, src, n, off, seed, cb), before in zip(G["segments"], segs, src_before):
+        want = []
+        for i, v in enumerate(c["dst_after"]):
+            if v == "r16":  # the one inexact sum: 1 + 2^-9
+                up = O.sr_r16(seed, cb + i) >= thr
+                want.append(0x3F81 if up else 0x3F80)
+            else:
+                want.append(int(v, 16))
+        assert dst.tolist() == want, c
+        if zero_src:
+            assert (src == 0).all()
+        else:
+            assert (src == before).all()
+
+
+def test_sr_segments_equal_the_per_tensor_loop():
+    """Random segments with distinct offsets, seeds and counter bases: the
+    segment loop equals, per tensor, the SR add of the slice followed by
+    clearing the whole reduced buffer."""
+    rng = np.random.default_rng(5)
+    segs, ref = [], []
+    for i in range(6):
+        ln = int(rng.integers(1, 40)) * 8
+        off = int(rng.integers(0, ln // 8)) * 8
+        n = int(rng.integers(0, ln - off + 1))
+        dst = (torch.randn(n + 3, generator=torch.Generator().manual_seed(i)) * 1e-2).to(
+            torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+        src = (torch.randn(ln, generator=torch.Generator().manual_seed(100 + i)) * 1e-4).to(
+            torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+        seed, cb = int(rng.integers(0, 2 ** 63)), int(rng.integers(0, 2 ** 40))
+        segs.append((dst, src, n, off, seed, cb))
+        ref.append((dst.copy(), src.copy(), n, off, seed, cb))
+    O.sr_accumulate_segments(segs, zero_src=True)
+    for (dst, src, n, off, seed, cb), (rd, rs, _, _, _, _) in zip(segs, ref):
+        O.sr_accumulate(rd[:n], rs[off:off + n].copy(), seed, cb)
+        rs[:] = 0
+        assert (dst == rd).all() and (src == rs).all()
+
+
+def test_oracle_rejects_bad_arguments():
+    g = np.zeros(64, np.float32)
+    for block in (0, 3, 8192):
+        with pytest.raises(ValueError):
+            O.quantize_ef_int4(g, None, block, 0.0, 1.0)
+    L = O.lib()
+    # called directly: NULL outputs and oversized blocks are refused, nothing written
+    assert L.orc_quantize_ef_int4(g.ctypes.data, 0, None, 64, 8192, 0.0, 1.0, None, None) != 0
+    assert L.orc_quantize_ef_int4(g.ctypes.data, 0, None, 64, 32, 0.0, 1.0, None, None) != 0
+    codes = np.full(64, -86, np.int8)
+    assert L.orc_quant_int8(g.ctypes.data, 0, 64, 4097, codes.ctypes.data, None) != 0
+    assert (codes == np.int8(-86)).all()
+    assert L.orc_zeropp_slots(0, 2, None) != 0

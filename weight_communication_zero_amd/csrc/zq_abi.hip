@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cstring>
 #include <vector>
 
 #include "../../include/zq.h"
@@ -31,13 +32,25 @@ size_t nblocks(size_t n, uint32_t block) { return (n + block - 1) / block; }
 
 zq_status launched(hipError_t e) { return e == hipSuccess ? ZQ_OK : ZQ_ERR_LAUNCH; }
 
+// The integer a C caller passed for an enum parameter.  Values outside the
+// enumerators are legal in C but not representable in the C++ enum type, so
+// they are read as bytes (memcpy), never as an enum value.
+template <typename E>
+int raw_enum(const E& e) {
+    static_assert(sizeof(E) == sizeof(int), "enums of the ABI are int-sized");
+    int v;
+    std::memcpy(&v, &e, sizeof v);
+    return v;
+}
+
 }  // namespace
 
 extern "C" {
 
-zq_status zq_quantize_ef_int4(const void* g, zq_dtype g_dtype, float* ef, size_t n, uint32_t block,
+zq_status zq_quantize_ef_int4(const void* g, zq_dtype g_dtype_arg, float* ef, size_t n, uint32_t block,
                               float beta_e, float beta_r, uint8_t* codes, float* scales,
                               void* stream) {
+    const int g_dtype = raw_enum(g_dtype_arg);
     if (g_dtype != ZQ_FP32 && g_dtype != ZQ_BF16)
         return ZQ_ERR_DTYPE;
     if (!valid_block(block))
@@ -59,10 +72,11 @@ zq_status zq_quantize_ef_int4(const void* g, zq_dtype g_dtype, float* ef, size_t
                                                 beta_r, codes, scales, (hipStream_t)stream));
 }
 
-zq_status zq_quantize_ef_int4_permuted(const void* g, zq_dtype g_dtype, float* ef, size_t n,
+zq_status zq_quantize_ef_int4_permuted(const void* g, zq_dtype g_dtype_arg, float* ef, size_t n,
                                        uint32_t block, float beta_e, float beta_r, uint8_t* codes,
                                        float* scales, uint32_t n_part,
                                        const uint32_t* slot_of_part, void* stream) {
+    const int g_dtype = raw_enum(g_dtype_arg);
     if (g_dtype != ZQ_FP32 && g_dtype != ZQ_BF16)
         return ZQ_ERR_DTYPE;
     if (!valid_block(block))
@@ -100,8 +114,9 @@ zq_status zq_quantize_ef_int4_permuted(const void* g, zq_dtype g_dtype, float* e
 }
 
 zq_status zq_quantize_ef_int4_batched(const zq_efq_segment* segs, uint32_t n_seg,
-                                      zq_dtype g_dtype, uint32_t block, float beta_e,
+                                      zq_dtype g_dtype_arg, uint32_t block, float beta_e,
                                       float beta_r, void* stream) {
+    const int g_dtype = raw_enum(g_dtype_arg);
     if (g_dtype != ZQ_FP32 && g_dtype != ZQ_BF16)
         return ZQ_ERR_DTYPE;
     if (!valid_block(block))
@@ -218,8 +233,9 @@ zq_status zq_dequant_reduce(uint32_t P, const uint8_t* const* codes, const float
     return launched(zq::launch_dequant_reduce(prm, block, (hipStream_t)stream));
 }
 
-zq_status zq_quant_int8(const void* w, zq_dtype w_dtype, size_t n, uint32_t block, int8_t* codes,
+zq_status zq_quant_int8(const void* w, zq_dtype w_dtype_arg, size_t n, uint32_t block, int8_t* codes,
                         float* scales, void* stream) {
+    const int w_dtype = raw_enum(w_dtype_arg);
     if (w_dtype != ZQ_FP32 && w_dtype != ZQ_BF16)
         return ZQ_ERR_DTYPE;
     if (!valid_block(block))
@@ -240,7 +256,8 @@ zq_status zq_quant_int8(const void* w, zq_dtype w_dtype, size_t n, uint32_t bloc
 }
 
 zq_status zq_dequant_int8(const int8_t* codes, const float* scales, size_t n, uint32_t block,
-                          void* out, zq_dtype out_dtype, void* stream) {
+                          void* out, zq_dtype out_dtype_arg, void* stream) {
+    const int out_dtype = raw_enum(out_dtype_arg);
     if (out_dtype != ZQ_FP32 && out_dtype != ZQ_BF16)
         return ZQ_ERR_DTYPE;
     if (!valid_block(block))
@@ -327,12 +344,23 @@ zq_status zq_sr_accumulate_batched(const zq_sr_segment* segs, uint32_t n_seg, in
                                                      zero_src != 0, (hipStream_t)stream));
 }
 
+uint32_t zq_zeropp_slots(uint32_t intra, uint32_t inter, uint32_t* slot_of_part) {
+    if (!slot_of_part || intra == 0 || inter == 0 || (uint64_t)intra * inter > zq::kMaxParts)
+        return 0;
+    // Local rank j receives slots j * inter .. j * inter + inter - 1 of every
+    // GPU in its node, and sends entry i of what it reduced to node i.
+    for (uint32_t j = 0; j < intra; ++j)
+        for (uint32_t i = 0; i < inter; ++i)
+            slot_of_part[i * intra + j] = j * inter + i;
+    return intra * inter;
+}
+
 size_t zq_int4_code_bytes(size_t n) { return n / 2 + (n & 1); }
 
 size_t zq_num_blocks(size_t n, uint32_t block) { return block ? nblocks(n, block) : 0; }
 
 const char* zq_status_str(zq_status s) {
-    switch (s) {
+    switch (raw_enum(s)) {
         case ZQ_OK: return "ZQ_OK";
         case ZQ_ERR_NULL: return "ZQ_ERR_NULL: a required pointer is NULL";
         case ZQ_ERR_SIZE: return "ZQ_ERR_SIZE: sizes inconsistent or too large";

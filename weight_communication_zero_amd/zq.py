@@ -71,6 +71,8 @@ def _load() -> C.CDLL:
     L.zq_quantize_ef_int4_batched.restype = i32
     L.zq_sr_accumulate_batched.argtypes = [vp, u32, i32, vp]
     L.zq_sr_accumulate_batched.restype = i32
+    L.zq_zeropp_slots.argtypes = [u32, u32, vp]
+    L.zq_zeropp_slots.restype = u32
     L.zq_int4_code_bytes.argtypes = [sz]
     L.zq_int4_code_bytes.restype = sz
     L.zq_num_blocks.argtypes = [sz, u32]
@@ -172,11 +174,14 @@ def zq_quantize_ef_int4(g, ef, block: int, beta_e: float, beta_r: float, codes, 
 
 
 def zeropp_slots(intra: int, inter: int) -> list[int]:
-    """ZeRO++'s partition order for `inter` nodes of `intra` GPUs: rank
-    r = node * intra + local owns partition r, which must sit in slot
-    local * inter + node for the intra-node then inter-node all-to-alls to
-    deliver it to rank r."""
-    return [(r % intra) * inter + r // intra for r in range(intra * inter)]
+    """ZeRO++'s partition order for `inter` nodes of `intra` GPUs, from
+    libzq's zq_zeropp_slots (slot_of_part[r] for rank r)."""
+    m = intra * inter
+    out = (C.c_uint32 * max(m, 1))()
+    got = lib.zq_zeropp_slots(intra, inter, out)
+    if got != m or m == 0:
+        raise ValueError(f"zq_zeropp_slots rejected intra={intra}, inter={inter}")
+    return list(out[:m])
 
 
 def zq_quantize_ef_int4_permuted(g, ef, block: int, beta_e: float, beta_r: float, codes, scales,
