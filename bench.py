@@ -218,6 +218,11 @@ def main():
     for name, k in (("efq_fp32_b128_7.5B", "efq"), ("dequant_reduce_requant_p8_b128_7.5B", "dr_rq"),
                     ("dequant_reduce_p4_b128_7.5B", "dr")):
         rows[name]["ms_p10_p50_p90"] = k_pct[k]
+    # counter-measured HBM bytes of the reduce-requant, while its profile is current
+    tr = measured_traffic("dequant_reduce_requant_p8_b128_7.5B", bytes_dr_rq)
+    rows["dequant_reduce_requant_p8_b128_7.5B"]["traffic"] = tr
+    rows["dequant_reduce_requant_p8_b128_7.5B"]["traffic_ratio"] = (
+        round(tr / bytes_dr_rq, 4) if tr else None)
 
     # ---------------------------------------------------- CPU baseline --
     cpu = None
@@ -233,7 +238,7 @@ def main():
 
     extras = not (args.no_rows or args.main_only)
     if extras:
-        rows.update(extra_rows(torch, zq, synth, dev, log))
+        rows.update(extra_rows(torch, zq, synth, dev, log, cpu=not args.no_cpu))
     ceil = ceilings(torch, dev) if extras else None
     if ceil:
         roofline["ceilings_measured"] = ceil
@@ -332,7 +337,32 @@ def variant_rows(torch, zq, g, ef, codes, scales, chunks_c, chunks_s, rq_codes, 
     table = zq.EfqSegmentTable(segs, B)
     ms_batched = timed(torch, lambda: zq.zq_quantize_ef_int4_batched(table, B, beta, 1.0), 10)
     del segs, table
+    # the receive side per parameter (LoCo's per-parameter reduce): tensor i's
+    # receive buffer holds its 8 peer chunks of n_i / 8 elements; each is
+    # reduced and requantized on its own, without and with a requant EF buffer
+    # per parameter
+    dsegs, dsegs_ef, off, roff = [], [], 0, 0
+    rq_ef = torch.zeros(n1, dtype=torch.float32, device=dev)
+    for t in tensors:
+        m = t.numel // P1
+        base = (codes[off // 2:(off + t.numel) // 2], scales[off // B:(off + t.numel) // B], m,
+                m // 2, m // B, None, rq_codes[roff // 2:(roff + m) // 2],
+                rq_scales[roff // B:(roff + m) // B])
+        dsegs.append(base + (None,))
+        dsegs_ef.append(base + (rq_ef[roff:roff + m],))
+        off += t.numel
+        roff += m
+    dtable = zq.DrSegmentTable(dsegs, P1, B)
+    dtable_ef = zq.DrSegmentTable(dsegs_ef, P1, B)
+    ms_drb = timed(torch, lambda: zq.zq_dequant_reduce_batched(dtable, P1, B, 1.0), 10)
+    ms_drb_ef = timed(torch, lambda: zq.zq_dequant_reduce_batched(dtable_ef, P1, B, 1.0, beta, 1.0),
+                      10)
+    del dsegs, dsegs_ef, dtable, dtable_ef, rq_ef
     return {
+        "dequant_reduce_requant_batched_327_tensors_p8_b128_7.5B": row(
+            dr_bytes(n1, B, P1, out=False, rq=True), ms_drb, n1),
+        "dequant_reduce_requant_ef_batched_327_tensors_p8_b128_7.5B": row(
+            dr_bytes(n1, B, P1, out=False, rq=True, rq_ef=True), ms_drb_ef, n1),
         "efq_batched_327_tensors_fp32_b128_7.5B": row(bytes_efq, ms_batched, M),
         "efq_permuted_zeropp_4x8_fp32_b128_7.5B": row(bytes_efq, ms_perm, M),
         "dequant_reduce_requant_ef_p8_b128_7.5B": row(
@@ -348,7 +378,11 @@ def row(nbytes, ms, elems):
 
 # The sources that define each profiled kernel: its counter summary stays
 # valid while these files are unchanged.
-KERNEL_SOURCES = {"efq_fp32_b128": ("zq_device.h", "zq_launch.h", "zq_efq.hip")}
+KERNEL_SOURCES = {
+    "efq_fp32_b128": ("zq_device.h", "zq_launch.h", "zq_efq.hip"),
+    "dequant_reduce_requant_p8_b128_7.5B": ("zq_device.h", "zq_launch.h", "zq_dr_launch.h",
+                                            "zq_dr_kernels.h", "zq_dr_b128_256.hip"),
+}
 
 
 def kernel_source_hash(kernel_tag):
@@ -414,6 +448,74 @@ def cpu_baseline(g_host, B, beta, P1, P2):
                         "dr": round(t3 - t2, 2)},
             "host": host_cpu_model() or platform.processor() or platform.machine(),
             "host_nproc": os.cpu_count(), "host_mem_gib": host_mem_gib()}
+
+
+def to_host_np(t):
+    """A device tensor as a host numpy array (bf16 as uint16 bit patterns)."""
+    import numpy as np
+    import torch
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def cpu_row(fn, nbytes, sample, split_of=None):
+    """The oracle (single-threaded, as written) timed once on a bounded
+    sample of a row's workload, in the row's own GB/s of algorithmic bytes.
+    fn returns the seconds of each of its stages when split_of names them."""
+    t0 = time.perf_counter()
+    parts = fn()
+    dt = time.perf_counter() - t0
+    out = {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": sample, "seconds": round(dt, 2)}
+    if split_of:
+        out["split_s"] = {k: round(v, 2) for k, v in zip(split_of, parts)}
+    return out
+
+
+def oracle_q8(w):
+    import oracle as O
+    t0 = time.perf_counter()
+    c, s = O.quant_int8(w, 2048)
+    t1 = time.perf_counter()
+    O.dequant_int8(c, s, 2048, out_bf16=True)
+    return t1 - t0, time.perf_counter() - t1
+
+
+def oracle_c4(g):
+    import numpy as np
+
+    import oracle as O
+    S = g.size
+    t0 = time.perf_counter()
+    c, s = O.quantize_ef_int4(g, np.zeros(S, np.float32), 128, 0.9, 1.0)
+    t1 = time.perf_counter()
+    n = S // 8
+    O.dequant_reduce([c[j * n // 2:(j + 1) * n // 2] for j in range(8)],
+                     [s[j * n // 128:(j + 1) * n // 128] for j in range(8)], n, 128, 0.125)
+    return t1 - t0, time.perf_counter() - t1
+
+
+def oracle_sr(src):
+    import numpy as np
+
+    import oracle as O
+    O.sr_accumulate(np.zeros(src.size, np.uint16), src.copy(), 0, 0)
+
+
+def oracle_c1(g):
+    import numpy as np
+
+    import oracle as O
+    n = g.size
+    t0 = time.perf_counter()
+    c, s = O.quantize_ef_int4(g, np.zeros(n, np.float32), 256, 1.0, 1.0)
+    t1 = time.perf_counter()
+    rank, nc = n // 4, n // 16
+    O.dequant_reduce([c[r * rank // 2:r * rank // 2 + nc // 2] for r in range(4)],
+                     [s[r * rank // 256:r * rank // 256 + nc // 256] for r in range(4)], nc, 256, 0.25)
+    return t1 - t0, time.perf_counter() - t1
 
 
 def host_cpu_model():
@@ -569,8 +671,10 @@ def cold_fields(nbytes, ms):
     return {"cold_ms": round(ms, 4), "cold_GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
-def extra_rows(torch, zq, synth, dev, log):
-    """The other rows of the path, each on its own workload."""
+def extra_rows(torch, zq, synth, dev, log, cpu=True):
+    """The other rows of the path, each on its own workload; with cpu, each
+    row also carries the oracle timed on a bounded sample of it."""
+    import ctypes as C
     rows = {}
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
     # qwZ: bf16 weights of the ~0.85B model, block 2048
@@ -586,6 +690,12 @@ def extra_rows(torch, zq, synth, dev, log):
     ms = timed_burst(torch, lambda: zq.zq_dequant_int8(c8, s8, 2048, wd), 20)
     rows["dequant_int8_bf16_b2048_0.85B"] = row(n * 3 + 4 * s8.numel(), ms, n)
     log("int8 rows", rows["quant_int8_bf16_b2048_0.85B"], rows["dequant_int8_bf16_b2048_0.85B"])
+    if cpu:
+        S = 1 << 27
+        wh = to_host_np(w[:S])
+        rows["quant_int8_bf16_b2048_0.85B"]["cpu_baseline"] = cpu_row(
+            lambda: oracle_q8(wh), 2 * (3 * S + 4 * S / 2048),
+            f"first {S} weights: int8 quantize then dequantize (bytes of both)", split_of=("q8", "dq8"))
     del w, c8, s8, wd
 
     # qgZ + LoCo on the ~0.85B fp32 gradient: EF quantize B=128 + 8-way reduce
@@ -603,6 +713,13 @@ def extra_rows(torch, zq, synth, dev, log):
     ms = timed_burst(torch, lambda: zq.zq_dequant_reduce(cc, ss, nc, 128, 0.125, out=outq), 20)
     rows["dequant_reduce_p8_b128_0.85B"] = row(dr_bytes(nc, 128, 8), ms, nc)
     log("0.85B qgZ rows", rows["efq_fp32_b128_0.85B"], rows["dequant_reduce_p8_b128_0.85B"])
+    if cpu:
+        S = 1 << 28
+        gh = to_host_np(gq[:S])
+        rows["efq_fp32_b128_0.85B"]["cpu_baseline"] = cpu_row(
+            lambda: oracle_c4(gh), efq_bytes(S, 128, 4) + dr_bytes(S // 8, 128, 8),
+            f"first {S} gradient elements: EF quantize + 8-way reduce of its {S // 8}-element "
+            "chunks (alpha 1/8)", split_of=("efq", "dr"))
     del gq, efq_, cq, sq, outq, cc, ss
 
     # llm.c ZeRO-2: SR accumulation of GPT-2 124M bf16 grads, full buffer and rank-3 shard
@@ -625,6 +742,11 @@ def extra_rows(torch, zq, synth, dev, log):
         row(6 * shard, ms, shard), **cold_fields(6 * shard, ms_c),
         note="93 MB: back-to-back calls run cache-resident; cold_* follow a 1 GiB write")
     log("SR rows", rows["sr_accumulate_bf16_gpt2_124M_full"])
+    if cpu:
+        S = 1 << 25
+        sh = to_host_np(src[:S])
+        rows["sr_accumulate_bf16_gpt2_124M_full"]["cpu_baseline"] = cpu_row(
+            lambda: oracle_sr(sh), 6 * S, f"first {S} elements of one micro-batch")
     del dst, src, dsh, ssh
 
     # llm.c's per-tensor ZeRO-2 loop for rank 3 of 8 over GPT-2's 148 tensors:
@@ -675,7 +797,27 @@ def extra_rows(torch, zq, synth, dev, log):
         row(efq_bytes(n, 256, 2), ms, n), **cold_fields(efq_bytes(n, 256, 2), ms_c),
         note="44 MB: back-to-back calls run cache-resident and launch-bound; cold_* follow a "
              "1 GiB write")
-    del flush
+    # ... and destination rank 0's 4-way reduce of chunk 0 of every rank (alpha 1/4)
+    nc, rank_n = n // 16, n // 4  # 2^18 elements per chunk, 2^20 per rank
+    out4 = torch.empty(nc, dtype=torch.float32, device=dev)
+    cp4 = (C.c_void_p * 4)(*[c4.data_ptr() + r * rank_n // 2 for r in range(4)])
+    sp4 = (C.c_void_p * 4)(*[s4.data_ptr() + 4 * (r * rank_n // 256) for r in range(4)])
+    op4 = out4.data_ptr()
+    dr4 = lambda: zq.lib.zq_dequant_reduce(4, cp4, sp4, nc, 256, 0.25, op4, None, None, None, 0.0,
+                                           1.0, st)
+    ms = timed_burst(torch, dr4, 200)
+    ms_c = timed_cold(torch, dr4, 20, flush)
+    rows["dequant_reduce_p4_b256_4x2^18"] = dict(
+        row(dr_bytes(nc, 256, 4), ms, nc), **cold_fields(dr_bytes(nc, 256, 4), ms_c),
+        note="2.2 MB: launch-bound; cold_* follow a 1 GiB write")
+    log("4-rank rows", rows["efq_bf16_b256_4x2^20"], rows["dequant_reduce_p4_b256_4x2^18"])
+    if cpu:
+        g4h = to_host_np(g4)
+        rows["efq_bf16_b256_4x2^20"]["cpu_baseline"] = cpu_row(
+            lambda: oracle_c1(g4h), efq_bytes(n, 256, 2) + dr_bytes(nc, 256, 4),
+            "the whole workload: EF quantize of the 4 ranks' 2^20 bf16 elements + the 4-way "
+            "reduce of chunk 0", split_of=("efq", "dr"))
+    del flush, out4
     torch.cuda.empty_cache()
     return rows
 

@@ -182,6 +182,51 @@ zq_status zq_dequant_reduce(uint32_t P, const uint8_t *const *codes, const float
                             float rq_beta_r, void *stream);
 
 /*
+ * zq_dequant_reduce_batched -- zq_dequant_reduce over many tensors in one
+ * call: DeepSpeed's LoCo path reduces what the all-to-all delivered
+ * parameter by parameter, each parameter with its own requant error-feedback
+ * buffer ([LoCo] review thread: all_to_all_loco_quant_reduce over the
+ * parameters to reduce, each with p.inter_ef_buf); here one pass covers all
+ * of them, up to 48 tensors per kernel launch (the table travels in the
+ * kernel arguments; nothing is allocated).
+ *
+ * Segment i is exactly zq_dequant_reduce(P, {codes + q * codes_stride},
+ * {scales + q * scales_stride}, n, block, alpha, out, rq_codes, rq_scales,
+ * rq_ef, rq_beta_e, rq_beta_r): peer q's chunk of the tensor starts
+ * codes_stride bytes and scales_stride floats after peer q - 1's, the layout
+ * an all-to-all receive buffer has.  Blocks restart at every segment and a
+ * segment's last block may be partial.
+ *   segs   HOST array of n_seg segments (read during the call only).
+ *          codes 16-byte aligned, codes_stride a multiple of 16 and at least
+ *          ceil(n/2) (any value when P == 1); scales 4-byte aligned,
+ *          scales_stride at least ceil(n/block); out, rq_codes, rq_ef
+ *          16-byte aligned, rq_scales 4-byte aligned.  out is NULL in every
+ *          non-empty segment or in none, and so are rq_codes (with rq_scales)
+ *          and rq_ef (only with rq_codes); at least one of out / rq_codes.
+ * Errors: ZQ_ERR_PEERS, ZQ_ERR_BLOCK; ZQ_ERR_NULL (segs NULL with n_seg > 0,
+ * a NULL input of a non-empty segment, outputs present in some segments
+ * only, or neither output); ZQ_ERR_SIZE (n_seg > 65536, a segment longer than
+ * 2^40 elements, a stride too short or above 2^50); ZQ_ERR_ALIGN;
+ * ZQ_ERR_ALIAS (any written range overlapping any input range or another
+ * written range of any segment; inputs may overlap each other).
+ */
+typedef struct {
+    const uint8_t *codes;
+    const float *scales;
+    uint64_t codes_stride;   /* bytes between peers' code chunks    */
+    uint64_t scales_stride;  /* floats between peers' scale chunks  */
+    uint64_t n;              /* elements per chunk                  */
+    float *out;
+    uint8_t *rq_codes;
+    float *rq_scales;
+    float *rq_ef;
+} zq_dr_segment;
+
+zq_status zq_dequant_reduce_batched(const zq_dr_segment *segs, uint32_t n_seg, uint32_t P,
+                                    uint32_t block, float alpha, float rq_beta_e, float rq_beta_r,
+                                    void *stream);
+
+/*
  * zq_quant_int8 -- qwZ: block int8 quantization of the weights before the
  * forward all-gather ([ZeRO++] section 1.2: fp16 to int8, an independent
  * quantization per block of parameters for accuracy).

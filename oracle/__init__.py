@@ -45,6 +45,9 @@ def lib():
         L.orc_zeropp_slots.restype = i32
         L.orc_dequant_reduce.argtypes = [u32, vp, vp, sz, u32, f32, vp, vp, vp, vp, f32, f32, vp]
         L.orc_dequant_reduce.restype = i32
+        L.orc_dequant_reduce_segments.argtypes = [u32, vp, vp, vp, vp, vp, vp, vp, vp, vp, u32, u32,
+                                                  f32, f32, f32, vp]
+        L.orc_dequant_reduce_segments.restype = i32
         L.orc_quant_int8.argtypes = [vp, i32, sz, u32, vp, vp]
         L.orc_quant_int8.restype = i32
         L.orc_dequant_int8.argtypes = [vp, vp, sz, u32, vp, i32]
@@ -165,6 +168,44 @@ def dequant_reduce(codes_list, scales_list, n_chunk: int, block: int, alpha: flo
     return out, rq_codes, rq_scales
 
 
+def dequant_reduce_segments(segments, P: int, block: int, alpha: float, want_out: bool = True,
+                            requant: bool = False, rq_efs=None, rq_beta_e: float = 0.0,
+                            rq_beta_r: float = 1.0):
+    """The receive side parameter by parameter ("Merge LoCo with Zero++",
+    review thread), done by the C oracle.  `segments`: (codes, scales, n,
+    codes_stride, scales_stride) with codes a uint8 array holding the P
+    chunks (peer p at byte p * codes_stride) and scales a float32 array
+    (peer p at element p * scales_stride).  rq_efs: one float32[n] per
+    segment (updated in place) or None.  Returns per segment (out or None,
+    rq_codes or None, rq_scales or None)."""
+    _check_block(block)
+    segs = list(segments)
+    m = len(segs)
+    cl = [np.ascontiguousarray(c, dtype=np.uint8) for c, _, _, _, _ in segs]
+    sl = [np.ascontiguousarray(s_, dtype=np.float32) for _, s_, _, _, _ in segs]
+    ns = [int(x[2]) for x in segs]
+    for c, s_, (_, _, n, cs, ss) in zip(cl, sl, segs):
+        if n:
+            assert c.size >= (P - 1) * cs + (n + 1) // 2 and s_.size >= (P - 1) * ss + num_blocks(n, block)
+    outs = [np.full(n, np.nan, np.float32) for n in ns] if want_out else None
+    rqc = [np.full(int4_code_bytes(n), _POISON_U8, np.uint8) for n in ns] if requant else None
+    rqs = [np.full(num_blocks(n, block), np.nan, np.float32) for n in ns] if requant else None
+    if rq_efs is not None:
+        assert requant and all(e.dtype == np.float32 and e.size == n for e, n in zip(rq_efs, ns))
+    arr = lambda lst: None if lst is None else (C.c_void_p * max(m, 1))(*[a.ctypes.data for a in lst])
+    u64 = lambda vals: np.array(list(vals) or [0], dtype=np.uint64)
+    work = np.empty(max(ns + [1]), np.float32)
+    # every array handed to C stays referenced until the call returns
+    cstride, sstride, n_arr = u64(x[3] for x in segs), u64(x[4] for x in segs), u64(ns)
+    tables = [arr(cl), arr(sl), arr(outs), arr(rqc), arr(rqs), arr(rq_efs)]
+    _ok(lib().orc_dequant_reduce_segments(
+        m, tables[0], tables[1], _ptr(cstride), _ptr(sstride), _ptr(n_arr), tables[2], tables[3],
+        tables[4], tables[5], P, block, alpha, rq_beta_e, rq_beta_r, _ptr(work)),
+        "dequant_reduce_segments")
+    return [((outs[i] if want_out else None), (rqc[i] if requant else None),
+             (rqs[i] if requant else None)) for i in range(m)]
+
+
 def quant_int8(w: np.ndarray, block: int):
     """qwZ int8 block quantization ([ZeRO++] notes, section 1.2).  w float32
     or uint16 (bf16 bits).  Returns (codes int8[n], scales float32[nb])."""
@@ -252,14 +293,15 @@ def sr_accumulate_segments(segments, zero_src: bool):
         assert dst.flags["C_CONTIGUOUS"] and src.flags["C_CONTIGUOUS"] and dst.size >= n
     ptrs = lambda arrs: (C.c_void_p * max(m, 1))(*[a.ctypes.data for a in arrs])
     u64s = lambda vals: np.array(list(vals) or [0], dtype=np.uint64)
+    # every array handed to C stays referenced until the call returns
     n = u64s(s[2] for s in segs)
     off = u64s(s[3] for s in segs)
     ln = u64s(s[1].size for s in segs)
     seed = u64s(s[4] for s in segs)
     cb = u64s(s[5] for s in segs)
-    _ok(lib().orc_sr_accumulate_segments(m, ptrs([s[0] for s in segs]), ptrs([s[1] for s in segs]),
-                                         _ptr(n), _ptr(off), _ptr(ln), _ptr(seed), _ptr(cb),
-                                         1 if zero_src else 0), "sr_accumulate_segments")
+    dsts, srcs = ptrs([s[0] for s in segs]), ptrs([s[1] for s in segs])
+    _ok(lib().orc_sr_accumulate_segments(m, dsts, srcs, _ptr(n), _ptr(off), _ptr(ln), _ptr(seed),
+                                         _ptr(cb), 1 if zero_src else 0), "sr_accumulate_segments")
 
 
 def zeropp_slots(intra: int, inter: int) -> list[int]:

@@ -27,7 +27,8 @@
  *
  * Parity status of each function (pins live in the CPU test suite):
  *   orc_quant_block, orc_quantize_ef_int4, orc_quantize_ef_int4_permuted,
- *   orc_zeropp_slots, orc_dequant_reduce, orc_quant_int8, orc_dequant_int8,
+ *   orc_zeropp_slots, orc_dequant_reduce, orc_dequant_reduce_segments,
+ *   orc_quant_int8, orc_dequant_int8,
  *   orc_bf16_rne, orc_sr_round, orc_philox4x32_10, orc_sr_accumulate,
  *   orc_sr_accumulate_segments, orc_volume_bytes: pinned.
  *
@@ -276,6 +277,43 @@ int orc_dequant_reduce(uint32_t P, const uint8_t *const *codes, const float *con
     if (rq_codes)
         return orc_quantize_ef_int4(work, 0, rq_ef, n_chunk, block, rq_beta_e, rq_beta_r, rq_codes,
                                     rq_scales);
+    return 0;
+}
+
+/* The receive side parameter by parameter ([LoCo] review thread: the LoCo
+ * path reduces each parameter's chunks separately, each with its own requant
+ * error-feedback buffer): segment i is the reduce above over P chunks of n[i]
+ * elements, peer p's chunk starting at codes[i] + p * cstride[i] bytes and
+ * scales[i] + p * sstride[i] floats, into out[i] and / or rq_codes[i],
+ * rq_scales[i], rq_ef[i] (any of these arrays may be NULL: no such output in
+ * any segment).  work holds the largest n[i] floats. */
+int orc_dequant_reduce_segments(uint32_t n_seg, const uint8_t *const *codes,
+                                const float *const *scales, const uint64_t *cstride,
+                                const uint64_t *sstride, const uint64_t *n, float *const *out,
+                                uint8_t *const *rq_codes, float *const *rq_scales,
+                                float *const *rq_ef, uint32_t P, uint32_t block, float alpha,
+                                float rq_beta_e, float rq_beta_r, float *work)
+{
+    if (n_seg > 0 && (!codes || !scales || !cstride || !sstride || !n || !work))
+        return ORC_EINVAL;
+    if (P < 1 || P > 64)
+        return ORC_EINVAL;
+    for (uint32_t i = 0; i < n_seg; i++) {
+        const uint8_t *cp[64];
+        const float *sp[64];
+        for (uint32_t p = 0; p < P; p++) {
+            cp[p] = codes[i] + p * cstride[i];
+            sp[p] = scales[i] + p * sstride[i];
+        }
+        if (n[i] == 0)
+            continue;
+        int rc = orc_dequant_reduce(P, cp, sp, n[i], block, alpha, out ? out[i] : NULL,
+                                    rq_codes ? rq_codes[i] : NULL,
+                                    rq_scales ? rq_scales[i] : NULL, rq_ef ? rq_ef[i] : NULL,
+                                    rq_beta_e, rq_beta_r, work);
+        if (rc)
+            return rc;
+    }
     return 0;
 }
 

@@ -54,6 +54,14 @@ hipError_t launch_dequant_reduce(const DrParams& p, uint32_t, hipStream_t) {
     launches++;
     return hipSuccess;
 }
+hipError_t launch_dequant_reduce_batched(const DrSegment* segs, uint32_t n_seg,
+                                         const DrBatchArgs& a, uint32_t, hipStream_t) {
+    CHECK(n_seg > 0 && a.P >= 1 && a.P <= kMaxPeers && (a.out || a.rq));
+    for (uint32_t i = 0; i < n_seg; ++i)
+        CHECK(segs[i].codes && segs[i].scales && segs[i].n > 0);
+    launches++;
+    return hipSuccess;
+}
 hipError_t launch_quant_int8(const void*, bool, size_t, uint32_t, int8_t*, float*, hipStream_t) {
     launches++;
     return hipSuccess;
@@ -147,7 +155,21 @@ int main() {
     ss[5].dst = ss[4].dst + 48;
     CHECK(zq_sr_accumulate_batched(ss.data(), S, 0, nullptr) == ZQ_ERR_ALIAS);
 
-    CHECK(launches == 8);
+    std::vector<zq_dr_segment> ds(S);
+    for (uint32_t i = 0; i < S; ++i) {
+        const uint64_t b = (uint64_t)i << 16;
+        ds[i] = {(const uint8_t*)fake(b), (const float*)fake(b + 0x2000), 256, 4, 512,
+                 nullptr, (uint8_t*)fake(b + 0x4000), (float*)fake(b + 0x6000),
+                 (float*)fake(b + 0x8000)};
+    }
+    CHECK(zq_dequant_reduce_batched(ds.data(), S, 8, 128, 1, 0.9f, 1, nullptr) == ZQ_OK);
+    ds[9].rq_ef = nullptr;
+    CHECK(zq_dequant_reduce_batched(ds.data(), S, 8, 128, 1, 0.9f, 1, nullptr) == ZQ_ERR_NULL);
+    ds[9].rq_ef = (float*)fake(((uint64_t)9 << 16) + 0x8000);
+    ds[11].rq_codes = (uint8_t*)fake(((uint64_t)12 << 16) + 0x100);  // inside 12's codes
+    CHECK(zq_dequant_reduce_batched(ds.data(), S, 8, 128, 1, 0.9f, 1, nullptr) == ZQ_ERR_ALIAS);
+
+    CHECK(launches == 9);
     for (int s = 0; s < 12; ++s)
         CHECK(zq_status_str((zq_status)s) != nullptr);
 #ifdef ZQ_SANITIZER_CANARY

@@ -18,7 +18,7 @@ def test_exports_every_declared_symbol():
     names = zq.declared_symbols()
     assert set(names) == {"zq_quantize_ef_int4", "zq_quantize_ef_int4_permuted",
                           "zq_quantize_ef_int4_batched",
-                          "zq_dequant_reduce", "zq_quant_int8",
+                          "zq_dequant_reduce", "zq_dequant_reduce_batched", "zq_quant_int8",
                           "zq_dequant_int8", "zq_sr_accumulate", "zq_sr_accumulate_batched",
                           "zq_int4_code_bytes", "zq_zeropp_slots",
                           "zq_num_blocks", "zq_status_str", "zq_abi_version"}
@@ -227,3 +227,47 @@ def test_efq_batched_validation():
     assert call([a, Seg(FAKE + 0x10000, FAKE + 0x1100000, FAKE + 0x200100, FAKE + 0x1300000, 64)]) \
         == zq.ZQ_ERR_ALIAS  # codes overlap
     assert call([Seg(FAKE, None, FAKE + 0x200000, FAKE + 0x300000, 0)]) == zq.ZQ_OK  # all empty
+
+
+def test_dequant_reduce_batched_validation():
+    Seg = zq.DrSegment
+
+    def call(segs, P=8, block=128, n_seg=None):
+        arr = (Seg * max(len(segs), 1))(*segs)
+        return L.zq_dequant_reduce_batched(C.cast(arr, C.c_void_p),
+                                           len(segs) if n_seg is None else n_seg, P, block, 1.0,
+                                           0.0, 1.0, None)
+
+    def seg(base, n=4096, out=True, rq=False, ef=False, cs=None, ss=None):
+        cs = n // 2 if cs is None else cs
+        ss = n // 128 if ss is None else ss
+        return Seg(base, base + 0x100000, cs, ss, n, base + 0x200000 if out else None,
+                   base + 0x300000 if rq else None, base + 0x340000 if rq else None,
+                   base + 0x380000 if ef else None)
+
+    a, b = seg(FAKE), seg(FAKE + 0x1000000)
+    assert call([a], P=0) == zq.ZQ_ERR_PEERS
+    assert call([a], P=17) == zq.ZQ_ERR_PEERS
+    assert call([a], block=48) == zq.ZQ_ERR_BLOCK
+    assert L.zq_dequant_reduce_batched(None, 0, 8, 128, 1.0, 0.0, 1.0, None) == zq.ZQ_OK
+    assert L.zq_dequant_reduce_batched(None, 3, 8, 128, 1.0, 0.0, 1.0, None) == zq.ZQ_ERR_NULL
+    assert call([a], n_seg=65537) == zq.ZQ_ERR_SIZE
+    assert call([seg(FAKE, n=(1 << 40) + 2)]) == zq.ZQ_ERR_SIZE
+    assert call([a, seg(FAKE + 0x1000000, out=False, rq=True)]) == zq.ZQ_ERR_NULL  # mixed outputs
+    assert call([seg(FAKE, out=False)]) == zq.ZQ_ERR_NULL                          # no output
+    assert call([seg(FAKE, ef=True)]) == zq.ZQ_ERR_NULL                            # EF without requant
+    assert call([Seg(None, FAKE, 2048, 32, 4096, FAKE + 0x200000, None, None, None)]) == zq.ZQ_ERR_NULL
+    assert call([seg(FAKE, cs=2047)]) == zq.ZQ_ERR_SIZE                            # stride too short
+    assert call([seg(FAKE, ss=31)]) == zq.ZQ_ERR_SIZE
+    assert call([seg(FAKE, cs=2056)]) == zq.ZQ_ERR_ALIGN                           # stride % 16
+    # for P = 1 the stride is not checked: this call gets as far as the alias check
+    assert call([Seg(FAKE, FAKE + 0x100000, 7, 0, 4096, FAKE + 0x400, None, None, None)],
+                P=1) == zq.ZQ_ERR_ALIAS
+    assert call([Seg(FAKE + 4, FAKE + 0x100000, 2048, 32, 4096, FAKE + 0x200000, None, None,
+                     None)]) == zq.ZQ_ERR_ALIGN
+    # the output of one segment inside the input chunks of another
+    assert call([a, Seg(FAKE + 0x1000000, FAKE + 0x1100000, 2048, 32, 4096, FAKE + 0x2000, None,
+                        None, None)]) == zq.ZQ_ERR_ALIAS
+    # two segments writing the same output
+    assert call([a, Seg(FAKE + 0x1000000, FAKE + 0x1100000, 2048, 32, 4096, FAKE + 0x200000, None,
+                        None, None)]) == zq.ZQ_ERR_ALIAS

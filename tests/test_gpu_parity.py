@@ -637,3 +637,119 @@ def test_requant_exact_ties(with_rq_ef):
     assert_bits_equal(rqs.host(), rqs_o, what + " scales")
     if with_rq_ef:
         assert_bits_equal(to_host(rq_ef), rq_ef_o, what + " rq_ef")
+
+
+# ----------------------------------------- batched dequantize + reduce --
+
+def _dr_segments(P, block, sizes, seed, raw):
+    """Per-tensor receive buffers: P chunks of n elements each, padded
+    strides (16-byte multiples for the codes), quantized gradients or raw
+    nibbles."""
+    rng = np.random.default_rng(seed)
+    segs = []
+    for i, n in enumerate(sizes):
+        cb, nb = (n + 1) // 2, -(-n // block)
+        cs = -(-cb // 16) * 16 + 16 * int(rng.integers(0, 3))
+        ss = nb + int(rng.integers(0, 3))
+        codes = rng.integers(0, 256, size=(P - 1) * cs + cb if n else 16, dtype=np.uint8)
+        scales = (rng.random((P - 1) * ss + nb if n else 1) * 1e-3).astype(np.float32)
+        if n and not raw:
+            chunks, chunk_scales = make_chunks(P, n, block, seed=seed * 100 + i)
+            for p in range(P):
+                codes[p * cs:p * cs + cb] = chunks[p]
+                scales[p * ss:p * ss + nb] = chunk_scales[p]
+        segs.append((codes, scales, n, cs, ss))
+    return segs
+
+
+def _run_dr_batched(segs, P, block, alpha, want_out, requant, with_ef, seed):
+    rng = np.random.default_rng(seed + 1)
+    efs = [(rng.standard_normal(s[2]) * 1e-6).astype(np.float32) for s in segs] if with_ef else None
+    efs_o = [e.copy() for e in efs] if with_ef else None  # updated in place by the oracle
+    ref = O.dequant_reduce_segments(segs, P, block, alpha, want_out=want_out, requant=requant,
+                                    rq_efs=efs_o, rq_beta_e=0.9, rq_beta_r=1.0)
+    bufs = []
+    table = []
+    for i, (codes, scales, n, cs, ss) in enumerate(segs):
+        cg, sg = to_gpu(codes), to_gpu(scales)
+        out = Guarded(max(n, 1), torch.float32) if want_out else None
+        rqc = Guarded(max((n + 1) // 2, 1), torch.uint8) if requant else None
+        rqs = Guarded(max(-(-n // block), 1), torch.float32) if requant else None
+        ef = to_gpu(efs[i]) if with_ef and n else None
+        bufs.append((cg, sg, out, rqc, rqs, ef))
+        table.append((cg, sg, n, cs, ss, out.t if out else None, rqc.t if rqc else None,
+                      rqs.t if rqs else None, ef))
+    Z().zq_dequant_reduce_batched(table, P, block, alpha, rq_beta_e=0.9, rq_beta_r=1.0)
+    torch.cuda.synchronize()
+    return ref, efs_o, bufs
+
+
+@pytest.mark.parametrize("block", [32, 128, 1024, 4096])
+@pytest.mark.parametrize("flags", [(True, False, False), (False, True, False), (False, True, True),
+                                   (True, True, True)])
+def test_dequant_reduce_batched_matches_oracle(block, flags):
+    """60 tensors (more than one launch takes) of ragged sizes -- empty,
+    shorter than a tile, several tiles plus a tail -- with padded strides,
+    against the oracle segment by segment, every output poisoned and
+    guarded."""
+    want_out, requant, with_ef = flags
+    tile = max(1024, block)
+    rng = np.random.default_rng(block)
+    sizes = [0, 1, block - 1, block, tile, tile + 3, 2 * tile + block // 2 + 1]
+    sizes += [int(rng.integers(1, 3 * tile)) for _ in range(60 - len(sizes))]
+    for P, raw in ((8, False), (3, True), (16, True), (1, False)):
+        segs = _dr_segments(P, block, sizes[: 60 if P == 8 else 20], seed=block + P, raw=raw)
+        ref, efs_o, bufs = _run_dr_batched(segs, P, block, 0.125 if P > 1 else 1.0, want_out, requant,
+                                           with_ef, seed=block * P)
+        for i, ((out_o, rqc_o, rqs_o), (cg, sg, out, rqc, rqs, ef), s) in enumerate(zip(ref, bufs, segs)):
+            n = s[2]
+            what = f"batched dr B={block} P={P} seg {i} n={n} flags={flags}"
+            if n == 0:
+                continue
+            if want_out:
+                assert_bits_equal(out.host()[:n], out_o, what + " out")
+            if requant:
+                assert_bits_equal(rqc.host(), rqc_o, what + " rq_codes")
+                assert_bits_equal(rqs.host(), rqs_o, what + " rq_scales")
+            if with_ef:
+                assert_bits_equal(to_host(ef), efs_o[i], what + " rq_ef")
+        for (cg, sg, out, rqc, rqs, ef), s in zip(bufs, segs):
+            if s[2] == 0:  # an empty segment writes nothing
+                for g in (out, rqc, rqs):
+                    if g is not None:
+                        v = to_host(g.buf)
+                        assert (v == 0xAA).all() if v.dtype == np.uint8 else np.isnan(v).all()
+
+
+def test_dequant_reduce_batched_equals_single_calls():
+    """The batched call against a loop of zq_dequant_reduce over the same
+    tensors (GPU against GPU), requant with EF, P = 8, block 128, including
+    two tensors that share one receive buffer."""
+    P, B = 8, 128
+    sizes = [4096, 1024 * 5 + 77, 512, 100000, 64, 1024]
+    segs = _dr_segments(P, B, sizes, seed=3, raw=False)
+    segs.append(segs[0])  # the same inputs reduced twice, into other outputs
+    rng = np.random.default_rng(4)
+    efs = [(rng.standard_normal(s[2]) * 1e-6).astype(np.float32) for s in segs]
+    outs_b, outs_s = [], []
+    table = []
+    for (codes, scales, n, cs, ss), e in zip(segs, efs):
+        cg, sg = to_gpu(codes), to_gpu(scales)
+        for dst, batched in ((outs_b, True), (outs_s, False)):
+            o = torch.empty(n, dtype=torch.float32, device="cuda")
+            rc = torch.empty((n + 1) // 2, dtype=torch.uint8, device="cuda")
+            rs = torch.empty(-(-n // B), dtype=torch.float32, device="cuda")
+            ef = to_gpu(e)
+            dst.append((o, rc, rs, ef))
+            if batched:
+                table.append((cg, sg, n, cs, ss, o, rc, rs, ef))
+            else:
+                Z().zq_dequant_reduce([cg[p * cs:p * cs + (n + 1) // 2] for p in range(P)],
+                                      [sg[p * ss:p * ss + -(-n // B)] for p in range(P)], n, B,
+                                      0.125, out=o, rq_codes=rc, rq_scales=rs, rq_ef=ef,
+                                      rq_beta_e=0.9, rq_beta_r=1.0)
+    Z().zq_dequant_reduce_batched(table, P, B, 0.125, rq_beta_e=0.9, rq_beta_r=1.0)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(outs_b, outs_s)):
+        for x, y, name in zip(a, b, ("out", "rq_codes", "rq_scales", "rq_ef")):
+            assert_bits_equal(to_host(x), to_host(y), f"segment {i} {name}")

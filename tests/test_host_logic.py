@@ -1,6 +1,7 @@
 """Host-side logic that needs no GPU: the build entry point, the benchmark's
 HBM-traffic lookup (valid only while the kernel source is unchanged since the
-counters were taken) and the pages' context figures in the benchmark line."""
+counters were taken), the build's refusal of kernels that use scratch memory,
+and the pages' context figures in the benchmark line."""
 import os
 import re
 import shutil
@@ -11,6 +12,15 @@ import bench
 from weight_communication_zero_amd import zq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _load_build():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "zq_build_for_test", os.path.join(ROOT, "weight_communication_zero_amd", "_build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
 
 
 def test_build_scripts_load_without_the_package():
@@ -59,3 +69,31 @@ def test_pages_context_counts_bytes_with_the_library_helpers():
     assert v["zeropp_int8_w2048_int4_g128"] == M + 4 * (M // 2048) + M // 2 + 4 * (M // 128)
     # the pages' 4x is the limit without scales; with them it is a bit less
     assert 3.9 < v["ratio"] < 4.0
+
+
+def test_build_refuses_kernels_that_use_scratch():
+    """The build parses the compiler's resource-usage remarks and names
+    every kernel with a nonzero scratch size."""
+    b = _load_build()
+    remarks = "\n".join([
+        "x.h:1:1: remark: Function Name: kern_a [-Rpass-analysis=kernel-resource-usage]",
+        "x.h:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "x.h:1:1: remark: Function Name: kern_b [-Rpass-analysis=kernel-resource-usage]",
+        "x.h:1:1: remark:     ScratchSize [bytes/lane]: 204 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert b.scratch_users(remarks) == [("kern_b", 204)]
+    assert b.scratch_users("") == []
+
+
+def test_requant_scale_division_is_exact_for_every_float(tmp_path):
+    """The reduce's requant computes its block scale fl(absmax / 7) as
+    q0 = a fl(1/7), e = fma(-q0, 7, a), q1 = fma(e, fl(1/7), q0): the same
+    bits as the IEEE division for every non-negative finite float, checked
+    exhaustively (2^31 values, split over the host's cores)."""
+    exe = str(tmp_path / "div_by_const")
+    r = subprocess.run(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-o", exe,
+                        os.path.join(ROOT, "tests", "arith", "div_by_const.c"), "-lm"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe, "7"], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0 and "0 mismatches" in r.stdout, r.stdout

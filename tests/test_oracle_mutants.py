@@ -77,6 +77,12 @@ MUTANTS = [
      "        if (n[i] > 0)\n            orc_sr_accumulate(dst[i], src[i] + off[i], n[i], seed[i], cbase[i], 0);"),
     ("segments: counter base taken from the offset", "seed[i], cbase[i], 0);", "seed[i], cbase[i] + off[i], 0);"),
     ("segments: one seed for all", "n[i], seed[i], cbase[i], 0);", "n[i], seed[0], cbase[i], 0);"),
+    ("reduce segments: scales stepped by the codes stride", "sp[p] = scales[i] + p * sstride[i];",
+     "sp[p] = scales[i] + p * cstride[i];"),
+    ("reduce segments: every peer reads peer 0", "cp[p] = codes[i] + p * cstride[i];",
+     "cp[p] = codes[i];"),
+    ("reduce segments: first segment's length for all", "int rc = orc_dequant_reduce(P, cp, sp, n[i], block,",
+     "int rc = orc_dequant_reduce(P, cp, sp, n[0], block,"),
 ]
 
 

@@ -759,3 +759,44 @@ def test_oracle_rejects_bad_arguments():
     assert L.orc_quant_int8(g.ctypes.data, 0, 64, 4097, codes.ctypes.data, None) != 0
     assert (codes == np.int8(-86)).all()
     assert L.orc_zeropp_slots(0, 2, None) != 0
+
+
+# ---------------------------------- per-parameter receive side (segments) --
+
+def test_dequant_reduce_segments_worked(golden_dir):
+    G = load(golden_dir, "dequant_reduce_segments_worked.json")
+    segs = [(hexbytes(c["codes"]), np.array(c["scales"], np.float32), c["n"], c["codes_stride"],
+             c["scales_stride"]) for c in G["segments"]]
+    res = O.dequant_reduce_segments(segs, G["P"], G["block"], G["alpha"], want_out=True,
+                                    requant=True)
+    for c, (out, rqc, rqs) in zip(G["segments"], res):
+        assert out.tolist() == c["out"], c
+        assert rqc.tolist() == hexbytes(c["rq_codes"]).tolist(), c
+        assert rqs.tolist() == c["rq_scales"], c
+
+
+def test_dequant_reduce_segments_equal_per_tensor_reduces():
+    """Random tensors of ragged sizes and padded strides: every segment
+    equals the plain reduce of its P chunks; requant EF per segment."""
+    rng = np.random.default_rng(9)
+    P, B = 3, 32
+    segs, chunks, efs = [], [], []
+    for i in range(5):
+        n = int(rng.integers(1, 300))
+        cs = (n + 1) // 2 + int(rng.integers(0, 5))
+        ss = -(-n // B) + int(rng.integers(0, 3))
+        codes = rng.integers(0, 256, size=(P - 1) * cs + (n + 1) // 2, dtype=np.uint8)
+        scales = (rng.random((P - 1) * ss + -(-n // B)) * 1e-3).astype(np.float32)
+        segs.append((codes, scales, n, cs, ss))
+        chunks.append(([codes[p * cs:p * cs + (n + 1) // 2] for p in range(P)],
+                       [scales[p * ss:p * ss + -(-n // B)] for p in range(P)], n))
+        efs.append((rng.standard_normal(n) * 1e-5).astype(np.float32))
+    efs_ref = [e.copy() for e in efs]
+    res = O.dequant_reduce_segments(segs, P, B, 0.25, want_out=True, requant=True, rq_efs=efs,
+                                    rq_beta_e=0.9, rq_beta_r=1.0)
+    for (cl, sl, n), (out, rqc, rqs), e_ref, e in zip(chunks, res, efs_ref, efs):
+        o2, c2, s2 = O.dequant_reduce(cl, sl, n, B, 0.25, want_out=True, requant=True, rq_ef=e_ref,
+                                      rq_beta_e=0.9, rq_beta_r=1.0)
+        assert (out.view(np.uint32) == o2.view(np.uint32)).all()
+        assert (rqc == c2).all() and (rqs.view(np.uint32) == s2.view(np.uint32)).all()
+        assert (e.view(np.uint32) == e_ref.view(np.uint32)).all()

@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import glob
 import os
+import re
 import subprocess
 import tempfile
 from concurrent.futures import ThreadPoolExecutor
@@ -39,12 +40,34 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+# Every kernel must run without private (scratch) memory: libzq promises
+# that it never has the runtime back anything for it.  The compiler's
+# resource-usage remarks name each kernel and its scratch bytes per lane.
+RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
+
+
+def scratch_users(stderr: str) -> list[tuple[str, int]]:
+    """(kernel, bytes per lane) of every kernel the remarks show using scratch."""
+    out, name = [], None
+    for line in stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0:
+            out.append((name, int(m.group(1))))
+    return out
+
+
 def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
-        print(" ".join(cmd), flush=True)
+        print(" ".join(c for c in cmd if c != RESOURCE_REMARKS), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr[-8000:]}")
+    users = scratch_users(r.stderr)
+    if users:
+        raise RuntimeError(f"kernels using scratch memory: {users}")
 
 
 def build(verbose: bool = False, extra: list[str] | None = None, out: str | None = None) -> str:
@@ -54,7 +77,8 @@ def build(verbose: bool = False, extra: list[str] | None = None, out: str | None
     tmp = out + ".tmp"
     with tempfile.TemporaryDirectory(prefix="zq_build_") as d:
         objs = [os.path.join(d, os.path.basename(s) + ".o") for s in sources()]
-        jobs = [[HIPCC, *FLAGS, *(extra or []), "-c", "-o", o, s] for s, o in zip(sources(), objs)]
+        jobs = [[HIPCC, *FLAGS, *(extra or []), RESOURCE_REMARKS, "-c", "-o", o, s]
+                for s, o in zip(sources(), objs)]
         with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1, 8)) as ex:
             for f in [ex.submit(_run, j, verbose) for j in jobs]:
                 f.result()

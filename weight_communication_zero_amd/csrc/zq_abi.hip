@@ -233,6 +233,88 @@ zq_status zq_dequant_reduce(uint32_t P, const uint8_t* const* codes, const float
     return launched(zq::launch_dequant_reduce(prm, block, (hipStream_t)stream));
 }
 
+zq_status zq_dequant_reduce_batched(const zq_dr_segment* segs, uint32_t n_seg, uint32_t P,
+                                    uint32_t block, float alpha, float rq_beta_e, float rq_beta_r,
+                                    void* stream) {
+    if (P < 1 || P > zq::kMaxPeers)
+        return ZQ_ERR_PEERS;
+    if (!valid_block(block))
+        return ZQ_ERR_BLOCK;
+    if (n_seg == 0)
+        return ZQ_OK;
+    if (!segs)
+        return ZQ_ERR_NULL;
+    if (n_seg > 65536)
+        return ZQ_ERR_SIZE;
+    struct Range {
+        uintptr_t lo, hi;
+        bool written;
+    };
+    std::vector<Range> ranges;
+    std::vector<zq::DrSegment> dev;
+    ranges.reserve(6 * (size_t)n_seg);
+    dev.reserve(n_seg);
+    int has_out = -1, has_rq = -1, has_ef = -1;  // unknown / 0 none / 1 all
+    const auto same = [](int& state, bool v) {
+        if (state >= 0 && state != (int)v)
+            return false;
+        state = v;
+        return true;
+    };
+    constexpr uint64_t kMaxStride = (uint64_t)1 << 50;
+    for (uint32_t i = 0; i < n_seg; ++i) {
+        const zq_dr_segment& g = segs[i];
+        if (g.n > kMaxSegElems)
+            return ZQ_ERR_SIZE;
+        if (g.n == 0)
+            continue;
+        if (!g.codes || !g.scales)
+            return ZQ_ERR_NULL;
+        if (!same(has_out, g.out != nullptr) || !same(has_rq, g.rq_codes != nullptr) ||
+            !same(has_ef, g.rq_ef != nullptr) || (g.rq_codes == nullptr) != (g.rq_scales == nullptr) ||
+            (g.rq_ef && !g.rq_codes) || (!g.out && !g.rq_codes))
+            return ZQ_ERR_NULL;
+        const size_t cb = zq_int4_code_bytes(g.n), nb = nblocks(g.n, block);
+        if (P > 1 && (g.codes_stride < cb || g.scales_stride < nb || g.codes_stride > kMaxStride ||
+                      g.scales_stride > kMaxStride))
+            return ZQ_ERR_SIZE;
+        if (!aligned(g.codes, 16) || !aligned(g.scales, 4) || (P > 1 && g.codes_stride % 16) ||
+            !aligned(g.out, 16) || !aligned(g.rq_codes, 16) || !aligned(g.rq_scales, 4) ||
+            !aligned(g.rq_ef, 16))
+            return ZQ_ERR_ALIGN;
+        const uint64_t cspan = (uint64_t)(P - 1) * (P > 1 ? g.codes_stride : 0) + cb;
+        const uint64_t sspan = 4 * ((uint64_t)(P - 1) * (P > 1 ? g.scales_stride : 0) + nb);
+        ranges.push_back({(uintptr_t)g.codes, (uintptr_t)g.codes + cspan, false});
+        ranges.push_back({(uintptr_t)g.scales, (uintptr_t)g.scales + sspan, false});
+        if (g.out)
+            ranges.push_back({(uintptr_t)g.out, (uintptr_t)g.out + 4 * g.n, true});
+        if (g.rq_codes) {
+            ranges.push_back({(uintptr_t)g.rq_codes, (uintptr_t)g.rq_codes + cb, true});
+            ranges.push_back({(uintptr_t)g.rq_scales, (uintptr_t)g.rq_scales + 4 * nb, true});
+        }
+        if (g.rq_ef)
+            ranges.push_back({(uintptr_t)g.rq_ef, (uintptr_t)g.rq_ef + 4 * g.n, true});
+        dev.push_back({g.codes, g.scales, P > 1 ? g.codes_stride : 0, P > 1 ? g.scales_stride : 0,
+                       g.n, g.out, g.rq_codes, g.rq_scales, g.rq_ef});
+    }
+    if (dev.empty())
+        return ZQ_OK;
+    std::sort(ranges.begin(), ranges.end(),
+              [](const Range& a, const Range& b) { return a.lo < b.lo; });
+    uintptr_t max_end_any = 0, max_end_written = 0;
+    for (const Range& r : ranges) {
+        if (r.lo < (r.written ? max_end_any : max_end_written))
+            return ZQ_ERR_ALIAS;
+        max_end_any = std::max(max_end_any, r.hi);
+        if (r.written)
+            max_end_written = std::max(max_end_written, r.hi);
+    }
+    const zq::DrBatchArgs a = {P, alpha, rq_beta_e, rq_beta_r, has_out == 1, has_rq == 1,
+                               has_ef == 1};
+    return launched(zq::launch_dequant_reduce_batched(dev.data(), (uint32_t)dev.size(), a, block,
+                                                      (hipStream_t)stream));
+}
+
 zq_status zq_quant_int8(const void* w, zq_dtype w_dtype_arg, size_t n, uint32_t block, int8_t* codes,
                         float* scales, void* stream) {
     const int w_dtype = raw_enum(w_dtype_arg);

@@ -212,8 +212,8 @@ __device__ __forceinline__ uint32_t load_code_word_masked(const uint8_t* p, size
 }
 
 // The code words and scales of every peer for one tile (see dr_tile).
-template <int B, int PMAX, bool RQ, bool EF, bool MASK>
-__device__ __forceinline__ void dr_load(const DrParams& p, size_t base,
+template <int B, int PMAX, bool RQ, bool EF, bool MASK, typename PV>
+__device__ __forceinline__ void dr_load(const PV& p, size_t base,
                                         uint32_t (&cw)[PMAX][DrGeomOf<B, RQ, EF>::U],
                                         float (&sc)[PMAX][DrGeomOf<B, RQ, EF>::U]) {
     using G = DrGeomOf<B, RQ, EF>;
@@ -230,16 +230,16 @@ __device__ __forceinline__ void dr_load(const DrParams& p, size_t base,
                 const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
                 if constexpr (BUF) {
                     const uint32_t le = (uint32_t)(u * G::SUB + lane * V);
-                    cw[q][u] = buf_load<code_word_t<V>, kBufLoadNT>(p.codes[q] + base / 2,
+                    cw[q][u] = buf_load<code_word_t<V>, kBufLoadNT>(p.codes_of(q) + base / 2,
                                                                     G::TILE / 2, le / 2);
-                    sc[q][u] = buf_load<float, 0>(p.scales[q] + base / B, G::TILE / B * 4,
+                    sc[q][u] = buf_load<float, 0>(p.scales_of(q) + base / B, G::TILE / B * 4,
                                                   4u * (le / B));
                 } else if constexpr (!MASK) {
-                    cw[q][u] = ld_stream((const code_word_t<V>*)(p.codes[q] + i0 / 2));
-                    sc[q][u] = p.scales[q][i0 / B];
+                    cw[q][u] = ld_stream((const code_word_t<V>*)(p.codes_of(q) + i0 / 2));
+                    sc[q][u] = p.scales_of(q)[i0 / B];
                 } else {
-                    cw[q][u] = load_code_word_masked<V / 2>(p.codes[q], i0 / 2, nbytes);
-                    sc[q][u] = i0 < n ? p.scales[q][i0 / B] : 0.0f;
+                    cw[q][u] = load_code_word_masked<V / 2>(p.codes_of(q), i0 / 2, nbytes);
+                    sc[q][u] = i0 < n ? p.scales_of(q)[i0 / B] : 0.0f;
                 }
             }
         }
@@ -249,8 +249,8 @@ __device__ __forceinline__ void dr_load(const DrParams& p, size_t base,
 // S = d_0 + d_1 + ..., ascending peer order, d = fl(k s) from the integer
 // nibble.  Peers are the outer loop so the runtime test q < P is one uniform
 // branch per peer, not a select per element.
-template <int PMAX, int U, int V>
-__device__ __forceinline__ void dr_sum_int(const DrParams& p, const uint32_t (&cw)[PMAX][U],
+template <int PMAX, int U, int V, typename PV>
+__device__ __forceinline__ void dr_sum_int(const PV& p, const uint32_t (&cw)[PMAX][U],
                                            const float (&sc)[PMAX][U], float (&R)[U][V]) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -275,8 +275,8 @@ __device__ __forceinline__ void dr_sum_int(const DrParams& p, const uint32_t (&c
 // block is infinite or NaN (a zero code gives 0 * inf = NaN) and so is every
 // sum of the block: the caller checks for that and redoes such a tile with
 // dr_sum_int.
-template <int PMAX, int U, int V>
-__device__ __forceinline__ void dr_sum_off(const DrParams& p, const uint32_t (&cw)[PMAX][U],
+template <int PMAX, int U, int V, typename PV>
+__device__ __forceinline__ void dr_sum_off(const PV& p, const uint32_t (&cw)[PMAX][U],
                                            const float (&sc)[PMAX][U], float (&R)[U][V]) {
     float f[V];
 #pragma unroll
@@ -305,15 +305,15 @@ __device__ __forceinline__ void dr_sum_off(const DrParams& p, const uint32_t (&c
 // dr_sum_int for one full tile, reloading the inputs one peer at a time in a
 // rolled loop: the rare redo path of the k / 16 decode, kept small so that
 // it adds no register pressure to the common path.
-template <int B, typename G>
-__device__ __forceinline__ void dr_sum_int_reload(const DrParams& p, size_t base,
+template <int B, typename G, typename PV>
+__device__ __forceinline__ void dr_sum_int_reload(const PV& p, size_t base,
                                                   float (&R)[G::U][G::VEC]) {
     constexpr int V = G::VEC;
     const int lane = lane_id();
 #pragma nounroll
     for (uint32_t q = 0; q < p.P; ++q) {
-        const uint8_t* codes = p.codes[q];
-        const float* scales = p.scales[q];
+        const uint8_t* codes = p.codes_of(q);
+        const float* scales = p.scales_of(q);
 #pragma unroll
         for (int u = 0; u < G::U; ++u) {
             const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
@@ -326,9 +326,35 @@ __device__ __forceinline__ void dr_sum_int_reload(const DrParams& p, size_t base
     }
 }
 
+// dr_sum_int for the ragged last tile: inputs past the chunk read as zero
+// (code bytes past ceil(n / 2), scales of blocks past n), one peer at a time
+// in a rolled loop so that no block size or peer count needs more registers
+// than one peer's words.
+template <int B, typename G, typename PV>
+__device__ __forceinline__ void dr_sum_masked(const PV& p, size_t base, float (&R)[G::U][G::VEC]) {
+    constexpr int V = G::VEC;
+    const int lane = lane_id();
+    const size_t n = p.n;
+    const size_t nbytes = (n + 1) / 2;
+#pragma nounroll
+    for (uint32_t q = 0; q < p.P; ++q) {
+        const uint8_t* codes = p.codes_of(q);
+        const float* scales = p.scales_of(q);
+#pragma unroll
+        for (int u = 0; u < G::U; ++u) {
+            const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * V;
+            const uint32_t w = load_code_word_masked<V / 2>(codes, i0 / 2, nbytes);
+            const float s = i0 < n ? scales[i0 / B] : 0.0f;
+#pragma unroll
+            for (int j = 0; j < V; ++j)
+                R[u][j] = q == 0 ? nib(w, j) * s : R[u][j] + nib(w, j) * s;
+        }
+    }
+}
+
 // R = alpha R, skipped for alpha = 1 (multiplying by one is the identity).
-template <int U, int V>
-__device__ __forceinline__ void dr_alpha(const DrParams& p, float (&R)[U][V]) {
+template <int U, int V, typename PV>
+__device__ __forceinline__ void dr_alpha(const PV& p, float (&R)[U][V]) {
     if (p.alpha != 1.0f) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -338,14 +364,38 @@ __device__ __forceinline__ void dr_alpha(const DrParams& p, float (&R)[U][V]) {
     }
 }
 
-// Requant input and block scales: c = R (+ the requant EF e2), in place;
-// elements past n are zeroed so that they do not enter the block max; then
-// the absmax of every block and its scale.
-template <int B, bool RQ, bool EF, bool MASK, typename G = DrGeomOf<B, RQ, EF>>
-__device__ __forceinline__ void rq_input(const DrParams& p, size_t base,
-                                         float (&c)[G::U][G::VEC],
-                                         const float (&e2)[G::U][G::VEC],
-                                         BlockScale (&bs)[G::SPB == 1 ? G::U : G::BPT]) {
+// Block scale of the requant: s = fl(a / 7) from q0 = a fl(1/7),
+// e = fma(-q0, 7, a) (exact), s = fma(e, fl(1/7), q0).  This equals the IEEE
+// quotient for every finite a >= 0, subnormals included (checked against
+// the IEEE division for all 2^31 non-negative finite floats); a = +inf or
+// NaN gives NaN, which the caller's non-finite-scale test sends to
+// rq_scales<..., true>, the IEEE division.  3 instructions instead of the
+// ~10 of the scaled divide sequence.
+#ifndef ZQ_DR_FAST_DIV
+#define ZQ_DR_FAST_DIV 1
+#endif
+template <int QMAX, bool EXACT>
+__device__ __forceinline__ BlockScale rq_block_scale(uint32_t amax_bits) {
+    if constexpr (EXACT || !ZQ_DR_FAST_DIV) {
+        return block_scale<QMAX>(amax_bits);
+    } else {
+        constexpr float r = 1.0f / (float)QMAX;
+        const float a = bitsf(amax_bits);
+        const float q0 = a * r;
+        const float e = __builtin_fmaf(-q0, (float)QMAX, a);
+        BlockScale b;
+        b.s = __builtin_fmaf(e, r, q0);
+        b.exact = (b.s != 0.0f) && (b.s < 0x1p-126f);
+        b.inv = (b.s == 0.0f) ? 0.0f : __builtin_amdgcn_rcpf(b.s);
+        return b;
+    }
+}
+
+// Requant input: c = R (+ the requant EF e2), in place; elements past n are
+// zeroed so that they do not enter the block max.
+template <int B, bool RQ, bool EF, bool MASK, typename G = DrGeomOf<B, RQ, EF>, typename PV>
+__device__ __forceinline__ void rq_compensate(const PV& p, size_t base, float (&c)[G::U][G::VEC],
+                                              const float (&e2)[G::U][G::VEC]) {
     constexpr int V = G::VEC;
     if constexpr (EF) {
 #pragma unroll
@@ -365,6 +415,13 @@ __device__ __forceinline__ void rq_input(const DrParams& p, size_t base,
                     c[u][j] = 0.0f;
         }
     }
+}
+
+// The absmax of every block of the requant input and its scale.
+template <int B, bool RQ, bool EF, bool EXACT, typename G = DrGeomOf<B, RQ, EF>>
+__device__ __forceinline__ void rq_scales(const float (&c)[G::U][G::VEC],
+                                          BlockScale (&bs)[G::SPB == 1 ? G::U : G::BPT]) {
+    constexpr int V = G::VEC;
     if constexpr (G::SPB == 1) {
 #pragma unroll
         for (int u = 0; u < G::U; ++u) {
@@ -372,7 +429,7 @@ __device__ __forceinline__ void rq_input(const DrParams& p, size_t base,
 #pragma unroll
             for (int j = 0; j < V; ++j)
                 m = max(m, absbits(c[u][j]));
-            bs[u] = block_scale<7>(group_max<G::LPB>(m));
+            bs[u] = rq_block_scale<7, EXACT>(group_max<G::LPB>(m));
         }
     } else {
 #pragma unroll
@@ -383,13 +440,13 @@ __device__ __forceinline__ void rq_input(const DrParams& p, size_t base,
 #pragma unroll
                 for (int j = 0; j < V; ++j)
                     m = max(m, absbits(c[u][j]));
-            bs[b] = block_scale<7>(group_max<kWave>(m));
+            bs[b] = rq_block_scale<7, EXACT>(group_max<kWave>(m));
         }
     }
 }
 
-template <int B, int PMAX, bool OUT, bool RQ, bool EF, bool MASK>
-__device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
+template <int B, int PMAX, bool OUT, bool RQ, bool EF, bool MASK, typename PV>
+__device__ __forceinline__ void dr_tile(const PV& p, size_t tile) {
     constexpr bool RQEF = RQ && EF;  // requant with its EF buffer (p.rq_ef)
     using G = DrGeomOf<B, RQ, EF>;
     constexpr int V = G::VEC;
@@ -402,8 +459,10 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
     float sc[PMAX][G::U];
     float e2[G::U][V];
 
-    // Issue every load of the tile first.
-    dr_load<B, PMAX, RQ, EF, MASK>(p, base, cw, sc);
+    // Issue every load of the tile first (the ragged tail instead loads and
+    // adds one peer at a time, below).
+    if constexpr (!MASK)
+        dr_load<B, PMAX, RQ, EF, MASK>(p, base, cw, sc);
     if constexpr (RQEF) {
 #pragma unroll
         for (int u = 0; u < G::U; ++u) {
@@ -430,7 +489,9 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
     // integer decode.
     constexpr bool OFFDEC = ZQ_DR_DECODE_OFF && RQ && !OUT && !MASK;
     float R[G::U][V];
-    if constexpr (OFFDEC)
+    if constexpr (MASK)
+        dr_sum_masked<B, G>(p, base, R);
+    else if constexpr (OFFDEC)
         dr_sum_off<PMAX, G::U, V>(p, cw, sc, R);
     else
         dr_sum_int<PMAX, G::U, V>(p, cw, sc, R);
@@ -463,7 +524,8 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
         // Compensated requant input, in place (R is not needed any more).
         float (&c)[G::U][V] = R;
         BlockScale bs[G::SPB == 1 ? G::U : G::BPT];
-        rq_input<B, RQ, EF, MASK>(p, base, c, e2, bs);
+        rq_compensate<B, RQ, EF, MASK>(p, base, c, e2);
+        rq_scales<B, RQ, EF, false>(c, bs);
         // Fast codes: rne(c * rcp(s)) by the 1.5 * 2^23 addition.  A tile
         // falls back to the IEEE quotient when an element is in the tie band
         // or a block scale is subnormal, infinite or NaN (uniform branch).
@@ -503,7 +565,8 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
                 if (__builtin_amdgcn_ballot_w64(bad) != 0) {
                     dr_sum_int_reload<B, G>(p, base, R);
                     dr_alpha<G::U, V>(p, R);
-                    rq_input<B, RQ, EF, MASK>(p, base, c, e2, bs);
+                    rq_compensate<B, RQ, EF, MASK>(p, base, c, e2);
+                    rq_scales<B, RQ, EF, false>(c, bs);
 #pragma unroll
                     for (int u = 0; u < G::U; ++u)
 #pragma unroll
@@ -511,6 +574,16 @@ __device__ __forceinline__ void dr_tile(const DrParams& p, size_t tile) {
                             kf[u][j] = code_fast_rne<7>(c[u][j], bs[G::SPB == 1 ? u : u / G::SPB],
                                                         bad);
                 }
+            }
+            if constexpr (ZQ_DR_FAST_DIV) {
+                // A non-finite absmax (outside the finite-input contract)
+                // takes the IEEE division, as the quantizer defines.
+                bool nonfinite = false;
+#pragma unroll
+                for (int b = 0; b < (G::SPB == 1 ? G::U : G::BPT); ++b)
+                    nonfinite |= !(bs[b].s <= 0x1.fffffep127f);
+                if (__builtin_amdgcn_ballot_w64(nonfinite) != 0)
+                    rq_scales<B, RQ, EF, true>(c, bs);
             }
 #pragma unroll
             for (int u = 0; u < G::U; ++u) {
@@ -639,11 +712,156 @@ hipError_t launch_peers(const DrParams& p, hipStream_t st) {
     return launch_flags<B, 16>(p, st);
 }
 
+// ---------------------------------------------------------------------------
+// Batched segments: the per-parameter receive side ("Merge LoCo with Zero++",
+// review thread: the LoCo path reduces parameter by parameter, each with its
+// own requant error-feedback buffer).  A launch takes up to kDrSegs segments
+// (the table rides in the kernel arguments); as in the batched EF quantize,
+// the first pass runs the full tiles of all segments, a wave finding its
+// segment by binary search over the cumulative tile counts, and the second
+// pass runs every segment's ragged last tile.
+#ifndef ZQ_DR_SEGS
+#define ZQ_DR_SEGS 48
+#endif
+constexpr int kDrSegs = ZQ_DR_SEGS;
+
+struct DrBatch {
+    DrSegment seg[kDrSegs];
+    uint32_t tile_end[kDrSegs];  // cumulative tiles through segment s
+    uint32_t nseg;
+    uint32_t total;
+    uint32_t P;
+    float alpha, rq_beta_e, rq_beta_r;
+};
+
+// A segment seen through the reduce tile's parameter interface.
+struct DrSegView {
+    const uint8_t* codes;
+    const float* scales;
+    uint64_t cstride, sstride;
+    uint32_t P;
+    size_t n;
+    float alpha;
+    float* out;
+    uint8_t* rq_codes;
+    float* rq_scales;
+    float* rq_ef;
+    float rq_beta_e, rq_beta_r;
+
+    __device__ const uint8_t* codes_of(uint32_t q) const { return codes + q * cstride; }
+    __device__ const float* scales_of(uint32_t q) const { return scales + q * sstride; }
+};
+
+__device__ __forceinline__ uint32_t find_dr_segment(const DrBatch& b, uint32_t t) {
+    uint32_t lo = 0, hi = b.nseg - 1;  // first s with t < tile_end[s]
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (t < b.tile_end[mid])
+            hi = mid;
+        else
+            lo = mid + 1;
+    }
+    return lo;
+}
+
+template <int B, int PMAX, bool OUT, bool RQ, bool EF, bool MASK>
+__global__ __launch_bounds__(kBlockThreads) void dr_batched_kernel(DrBatch b) {
+    using G = DrGeomOf<B, RQ, EF>;
+    for (size_t ts = wave_id(); ts < b.total; ts += wave_count()) {
+        const uint32_t t = (uint32_t)ts;
+        const uint32_t s = find_dr_segment(b, t);
+        const DrSegment& g = b.seg[s];
+        const DrSegView v = {g.codes,    g.scales,    g.codes_stride, g.scales_stride, b.P,
+                             g.n,        b.alpha,     g.out,          g.rq_codes,      g.rq_scales,
+                             g.rq_ef,    b.rq_beta_e, b.rq_beta_r};
+        // full tiles: the local index within the segment; tails: its last tile
+        const size_t local = MASK ? g.n / G::TILE : t - (s ? b.tile_end[s - 1] : 0u);
+        dr_tile<B, PMAX, OUT, RQ, EF, MASK>(v, local);
+    }
+}
+
+template <int B, int PMAX, bool OUT, bool RQ, bool EF>
+hipError_t launch_batched_b(const DrSegment* segs, uint32_t n_seg, const DrBatchArgs& a,
+                            hipStream_t stream) {
+    using G = DrGeomOf<B, RQ, EF>;
+    static_assert(G::TILE >= 512, "2^40-element segments need tiles of >= 512");
+    const Geometry geom = (RQ && !EF) ? kGeomReduceRequant : kGeomReduce;
+    for (int pass = 0; pass < 2; ++pass) {  // 0: full tiles, 1: ragged last tiles
+        uint32_t i = 0;
+        while (i < n_seg) {
+            DrBatch bt = {};
+            bt.P = a.P;
+            bt.alpha = a.alpha;
+            bt.rq_beta_e = a.rq_beta_e;
+            bt.rq_beta_r = a.rq_beta_r;
+            uint64_t tiles = 0;
+            // A launch takes segments while its tile count (32-bit in the
+            // kernel's table) stays below 2^32.
+            while (i < n_seg && bt.nseg < (uint32_t)kDrSegs) {
+                const DrSegment& g = segs[i];
+                const uint64_t t = pass == 0 ? g.n / G::TILE : (g.n % G::TILE ? 1 : 0);
+                if (tiles + t > UINT32_MAX)
+                    break;  // the next launch starts with this segment
+                ++i;
+                if (t == 0)
+                    continue;
+                bt.seg[bt.nseg] = g;
+                tiles += t;
+                bt.tile_end[bt.nseg++] = (uint32_t)tiles;
+            }
+            if (bt.nseg == 0)
+                continue;
+            bt.total = (uint32_t)tiles;
+            void* args[] = {(void*)&bt};
+            const void* fn = pass == 0 ? (const void*)&dr_batched_kernel<B, PMAX, OUT, RQ, EF, false>
+                                       : (const void*)&dr_batched_kernel<B, PMAX, OUT, RQ, EF, true>;
+            const Geometry g = pass == 0 ? geom : Geometry{kWave, 1u << 22};
+            const hipError_t e = hipLaunchKernel(fn, grid_for_tiles(tiles, g), dim3(g.threads),
+                                                 args, 0, stream);
+            if (e != hipSuccess)
+                return e;
+        }
+    }
+    return hipSuccess;
+}
+
+template <int B, int PMAX>
+hipError_t launch_batched_flags(const DrSegment* segs, uint32_t n_seg, const DrBatchArgs& a,
+                                hipStream_t st) {
+    if (a.out && !a.rq)
+        return launch_batched_b<B, PMAX, true, false, false>(segs, n_seg, a, st);
+    if (!a.out && a.rq)
+        return a.rq_ef ? launch_batched_b<B, PMAX, false, true, true>(segs, n_seg, a, st)
+                       : launch_batched_b<B, PMAX, false, true, false>(segs, n_seg, a, st);
+    if (a.out && a.rq)
+        return a.rq_ef ? launch_batched_b<B, PMAX, true, true, true>(segs, n_seg, a, st)
+                       : launch_batched_b<B, PMAX, true, true, false>(segs, n_seg, a, st);
+    return hipErrorInvalidValue;
+}
+
+template <int B>
+hipError_t launch_batched_peers(const DrSegment* segs, uint32_t n_seg, const DrBatchArgs& a,
+                                hipStream_t st) {
+    if (a.P <= 2)
+        return launch_batched_flags<B, 2>(segs, n_seg, a, st);
+    if (a.P <= 4)
+        return launch_batched_flags<B, 4>(segs, n_seg, a, st);
+    if (a.P <= 8)
+        return launch_batched_flags<B, 8>(segs, n_seg, a, st);
+    return launch_batched_flags<B, 16>(segs, n_seg, a, st);
+}
+
 }  // namespace
 
 // One launcher per block size, each compiled in its own translation unit
-// (zq_dr_b*.hip) so that the instantiations build in parallel.
+// (zq_dr_b*.hip for single calls, zq_drb_b*.hip for batched ones) so that
+// the instantiations build in parallel.
 #define ZQ_DR_LAUNCHER(BLK) \
     hipError_t launch_dr_b##BLK(const DrParams& p, hipStream_t st) { return launch_peers<BLK>(p, st); }
+#define ZQ_DRB_LAUNCHER(BLK)                                                                  \
+    hipError_t launch_drb_b##BLK(const DrSegment* segs, uint32_t n_seg, const DrBatchArgs& a, \
+                                 hipStream_t st) {                                             \
+        return launch_batched_peers<BLK>(segs, n_seg, a, st);                                  \
+    }
 
 }  // namespace zq

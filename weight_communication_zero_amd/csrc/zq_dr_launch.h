@@ -16,4 +16,17 @@ hipError_t launch_dr_b1024(const DrParams& p, hipStream_t st);
 hipError_t launch_dr_b2048(const DrParams& p, hipStream_t st);
 hipError_t launch_dr_b4096(const DrParams& p, hipStream_t st);
 
+#define ZQ_DRB_DECL(BLK)                                                                  \
+    hipError_t launch_drb_b##BLK(const DrSegment* segs, uint32_t n_seg, const DrBatchArgs& a, \
+                                 hipStream_t st);
+ZQ_DRB_DECL(32)
+ZQ_DRB_DECL(64)
+ZQ_DRB_DECL(128)
+ZQ_DRB_DECL(256)
+ZQ_DRB_DECL(512)
+ZQ_DRB_DECL(1024)
+ZQ_DRB_DECL(2048)
+ZQ_DRB_DECL(4096)
+#undef ZQ_DRB_DECL
+
 }  // namespace zq

@@ -92,9 +92,39 @@ struct DrParams {
     float* rq_ef;
     float rq_beta_e;
     float rq_beta_r;
+
+    __device__ const uint8_t* codes_of(uint32_t q) const { return codes[q]; }
+    __device__ const float* scales_of(uint32_t q) const { return scales[q]; }
 };
 
 hipError_t launch_dequant_reduce(const DrParams& p, uint32_t block, hipStream_t stream);
+
+// One tensor of a batched dequantize-reduce (validated by the ABI layer):
+// peer q's chunk of n elements has its codes at codes + q * codes_stride
+// bytes and its scales at scales + q * scales_stride floats.
+struct DrSegment {
+    const uint8_t* codes;
+    const float* scales;
+    uint64_t codes_stride;
+    uint64_t scales_stride;
+    uint64_t n;
+    float* out;
+    uint8_t* rq_codes;
+    float* rq_scales;
+    float* rq_ef;
+};
+
+// Settings shared by every segment of a batch.
+struct DrBatchArgs {
+    uint32_t P;
+    float alpha;
+    float rq_beta_e;
+    float rq_beta_r;
+    bool out, rq, rq_ef;
+};
+
+hipError_t launch_dequant_reduce_batched(const DrSegment* segs, uint32_t n_seg,
+                                         const DrBatchArgs& a, uint32_t block, hipStream_t stream);
 
 hipError_t launch_quant_int8(const void* w, bool w_bf16, size_t n, uint32_t block, int8_t* codes,
                              float* scales, hipStream_t stream);

@@ -43,6 +43,13 @@ class EfqSegment(C.Structure):
                 ("scales", C.c_void_p), ("n", C.c_uint64)]
 
 
+class DrSegment(C.Structure):
+    """zq_dr_segment of include/zq.h."""
+    _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("codes_stride", C.c_uint64),
+                ("scales_stride", C.c_uint64), ("n", C.c_uint64), ("out", C.c_void_p),
+                ("rq_codes", C.c_void_p), ("rq_scales", C.c_void_p), ("rq_ef", C.c_void_p)]
+
+
 class ZQError(RuntimeError):
     def __init__(self, fn: str, status: int):
         super().__init__(f"{fn} failed: {lib.zq_status_str(status).decode()}")
@@ -69,6 +76,8 @@ def _load() -> C.CDLL:
     L.zq_quantize_ef_int4_permuted.restype = i32
     L.zq_quantize_ef_int4_batched.argtypes = [vp, u32, i32, u32, f32, f32, vp]
     L.zq_quantize_ef_int4_batched.restype = i32
+    L.zq_dequant_reduce_batched.argtypes = [vp, u32, u32, u32, f32, f32, f32, vp]
+    L.zq_dequant_reduce_batched.restype = i32
     L.zq_sr_accumulate_batched.argtypes = [vp, u32, i32, vp]
     L.zq_sr_accumulate_batched.restype = i32
     L.zq_zeropp_slots.argtypes = [u32, u32, vp]
@@ -314,3 +323,37 @@ def zq_quantize_ef_int4_batched(segments, block: int, beta_e: float, beta_r: flo
            lib.zq_quantize_ef_int4_batched(table.ptr, len(table.segments),
                                            ZQ_FP32 if table.dtype is None else table.dtype, block,
                                            beta_e, beta_r, _stream(stream)))
+
+
+class DrSegmentTable:
+    """A marshalled segment table for zq_dequant_reduce_batched.  Each
+    segment is (codes, scales, n, codes_stride, scales_stride, out, rq_codes,
+    rq_scales, rq_ef): codes a uint8 tensor holding the P peer chunks (peer q
+    at byte q * codes_stride), scales a float32 tensor (peer q at element
+    q * scales_stride); outputs as in zq_dequant_reduce (None for absent)."""
+
+    def __init__(self, segments, P: int, block: int):
+        self.segments = list(segments)
+        self.arr = (DrSegment * max(len(self.segments), 1))()
+        nbk = lambda n: (n + block - 1) // block
+        for i, (codes, scales, n, cst, sst, out, rqc, rqs, rqe) in enumerate(self.segments):
+            _need("codes", codes, (P - 1) * cst + (n + 1) // 2 if n else 0, _U8)
+            _need("scales", scales, (P - 1) * sst + nbk(n) if n else 0, _F32)
+            _need("out", out, n, _F32)
+            _need("rq_codes", rqc, (n + 1) // 2, _U8)
+            _need("rq_scales", rqs, nbk(n), _F32)
+            _need("rq_ef", rqe, n, _F32)
+            self.arr[i] = DrSegment(_p(codes), _p(scales), cst, sst, n, _p(out), _p(rqc), _p(rqs),
+                                    _p(rqe))
+        self.P, self.block = P, block
+        self.ptr = C.cast(self.arr, C.c_void_p)
+
+
+def zq_dequant_reduce_batched(segments, P: int, block: int, alpha: float, rq_beta_e: float = 0.0,
+                              rq_beta_r: float = 1.0, stream=None) -> None:
+    """Per-tensor dequantize-reduce(-requant) of many tensors in one call:
+    `segments` is a DrSegmentTable or an iterable of its tuples."""
+    table = segments if isinstance(segments, DrSegmentTable) else DrSegmentTable(segments, P, block)
+    _check("zq_dequant_reduce_batched",
+           lib.zq_dequant_reduce_batched(table.ptr, len(table.segments), P, block, alpha, rq_beta_e,
+                                         rq_beta_r, _stream(stream)))
