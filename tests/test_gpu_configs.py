@@ -58,6 +58,17 @@ def int4_block_bytes(codes: torch.Tensor, blocks: np.ndarray, B: int) -> np.ndar
     return gather_blocks(codes, blocks, B // 2)
 
 
+def assert_sr_brackets(out: torch.Tensor, x: torch.Tensor, what: str):
+    """Every stochastically rounded bf16 output is x truncated toward zero
+    (its top 16 bits) or the next bf16 away from zero (one more), and x
+    itself when bf16 holds it exactly -- over the whole buffer."""
+    xb = x.view(torch.int32).to(torch.int64) & 0xFFFFFFFF
+    ob = out.view(torch.int16).to(torch.int64) & 0xFFFF
+    d = ob - (xb >> 16)
+    assert bool(((d == 0) | (d == 1)).all()), f"{what}: a result outside [RZ(x), RZ(x) + 1 ulp]"
+    assert bool((d[(xb & 0xFFFF) == 0] == 0).all()), f"{what}: a representable sum moved"
+
+
 # ------------------------------------------------------------------ 4 ranks --
 
 def test_four_ranks_bf16_block256_full_compare():
@@ -112,7 +123,10 @@ def test_gpt2_sr_accumulation_full_buffer_and_rank3_shard():
     for m in range(8):
         synth.fill_model(src, tensors, std=1e-4, seed=synth.seed_for("gpt2", "grad", mb=m))
         src_host = {int(s0): to_host(src[s0:s0 + W]).copy() for s0 in starts}
+        x = dst.float() + src.float()  # the fp32 sum (round to nearest) the kernel rounds
         Z().zq_sr_accumulate(dst, src, seed=m, counter_base=0)
+        assert_sr_brackets(dst, x, f"GPT-2 full buffer, micro-batch {m}")
+        del x
         Z().zq_sr_accumulate(dsh, src[off:off + shard], seed=m, counter_base=off)
         for s0 in starts:
             O.sr_accumulate(win_o[int(s0)], src_host[int(s0)], seed=m, counter_base=int(s0))
@@ -121,6 +135,61 @@ def test_gpt2_sr_accumulation_full_buffer_and_rank3_shard():
         "rank-3 shard differs from the same slice of the full-buffer accumulation"
     for s0 in starts:
         assert_bits_equal(to_host(dst[s0:s0 + W]), win_o[int(s0)], f"SR window at {s0}")
+
+
+
+def test_sr_past_the_xcd_ordered_map_single_and_batched():
+    """SR over 3 full blocks of 131,072 one-tile workgroups (where the
+    streaming kernels take XCD-contiguous runs), a trailing partial block of
+    12,345 workgroups in dispatch order and a ragged last tile of 333
+    elements.  First call: dst = 0, so every output must equal its src value
+    exactly (a tile skipped or visited twice shows); second call: windows
+    against the oracle at the first and last tiles and on both sides of
+    every run boundary, and the bracketing property over the whole buffer;
+    zero_src must clear all of src.  Then the same through the batched entry
+    point, as one large segment plus a small one."""
+    tile, run = 1024, 131072
+    n = 3 * run * tile + 12345 * tile + 333
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    src = torch.randn(n, device="cuda", generator=gen).to(torch.bfloat16)
+    dst = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    Z().zq_sr_accumulate(dst, src, seed=1, counter_base=0)
+    torch.cuda.synchronize()
+    assert torch.equal(dst.view(torch.int16), src.view(torch.int16)), "a tile was missed or repeated"
+    W = 1024
+    edges = [0, n - W, n - 333 - W]
+    for b in range(1, 4):
+        edges += [b * run * tile - W, b * run * tile]
+        edges += [(b - 1) * run * tile + x * 16384 * tile + o for x in range(1, 8) for o in (-W, 0)]
+    rng = np.random.default_rng(12)
+    edges += list(rng.integers(0, n - W, size=24))
+    starts = sorted(set(int(e) for e in edges))
+    src2 = (torch.randn(n, device="cuda", generator=gen) * 1e-2).to(torch.bfloat16)
+    win_d = {s0: to_host(dst[s0:s0 + W]).copy() for s0 in starts}
+    win_s = {s0: to_host(src2[s0:s0 + W]).copy() for s0 in starts}
+    x = dst.float() + src2.float()
+    Z().zq_sr_accumulate(dst, src2, seed=(1 << 40) + 7, counter_base=3, zero_src=True)
+    torch.cuda.synchronize()
+    assert_sr_brackets(dst, x, "large SR")
+    del x
+    assert int(torch.count_nonzero(src2.view(torch.int16))) == 0, "zero_src left src elements"
+    for s0 in starts:
+        O.sr_accumulate(win_d[s0], win_s[s0], seed=(1 << 40) + 7, counter_base=3 + s0)
+        assert_bits_equal(to_host(dst[s0:s0 + W]), win_d[s0], f"large SR window at {s0}")
+    # batched: one large segment and one small one, reduced buffers cleared
+    small = 5000
+    dst_b = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    dst_s = torch.zeros(small, dtype=torch.bfloat16, device="cuda")
+    red_s = torch.randn(4 * small, device="cuda", generator=gen).to(torch.bfloat16)
+    want_s = red_s[2 * small:3 * small].clone()
+    src3 = src.clone()
+    Z().zq_sr_accumulate_batched([(dst_b, src3, n, 0, 9, 0), (dst_s, red_s, small, 2 * small, 10, 77)],
+                                 zero_src=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dst_b.view(torch.int16), src.view(torch.int16)), "batched: tile missed or repeated"
+    assert torch.equal(dst_s.view(torch.int16), want_s.view(torch.int16))
+    assert int(torch.count_nonzero(src3.view(torch.int16))) == 0
+    assert int(torch.count_nonzero(red_s.view(torch.int16))) == 0
 
 
 # ------------------------------------------------------------ qwZ 0.85B --
@@ -366,3 +435,68 @@ def test_per_tensor_batched_quantize_equals_flat_call_0p85b():
         assert torch.equal(ca, cb), f"step {step} codes"
         assert torch.equal(sa.view(torch.int32), sb.view(torch.int32)), f"step {step} scales"
         assert torch.equal(ef_a.view(torch.int32), ef_b.view(torch.int32)), f"step {step} ef"
+
+
+# ------------------------------------- per-parameter receive side, 7.5B --
+
+def test_per_tensor_batched_reduce_requant_7p5b_sampled():
+    """The receive side parameter by parameter over the ~7.5B model's 327
+    tensors: tensor i's receive buffer holds its 8 peer chunks of n_i / 8
+    elements (contiguous, as an all-to-all delivers them), each reduced and
+    requantized on its own with its own requant EF buffer, 2 steps -- one
+    zq_dequant_reduce_batched call per step.  Whole outputs poisoned and
+    checked written; the first and last output block of every tensor and
+    random others recomputed by the oracle from the generator's inputs."""
+    tensors = synth.llama_7p5b()
+    M = synth.total(tensors)
+    B, P = 128, 8
+    n1 = M // P
+    g = torch.empty(M, dtype=torch.float32, device="cuda")
+    codes = torch.empty(M // 2, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(M // B, dtype=torch.float32, device="cuda")
+    rqc = torch.empty(n1 // 2, dtype=torch.uint8, device="cuda")
+    rqs = torch.empty(n1 // B, dtype=torch.float32, device="cuda")
+    rq_ef = torch.zeros(n1, dtype=torch.float32, device="cuda")
+    segs, where, off, roff = [], [], 0, 0
+    for t in tensors:
+        m = t.numel // P
+        segs.append((codes[off // 2:(off + t.numel) // 2], scales[off // B:(off + t.numel) // B], m,
+                     m // 2, m // B, None, rqc[roff // 2:(roff + m) // 2], rqs[roff // B:(roff + m) // B],
+                     rq_ef[roff:roff + m]))
+        where.append((off, roff, m))
+        off += t.numel
+        roff += m
+    table = Z().DrSegmentTable(segs, P, B)
+    rng = np.random.default_rng(21)
+    # tracked output blocks: (segment, block within the segment)
+    picks = []
+    for i, (_, _, m) in enumerate(where):
+        picks += [(i, 0), (i, m // B - 1)]
+    for i in rng.integers(0, len(where), size=200):
+        picks.append((int(i), int(rng.integers(0, where[i][2] // B))))
+    picks = sorted(set(picks))
+    out_blocks = np.array([where[i][1] // B + b for i, b in picks])
+    in_blocks = np.array([(where[i][0] + j * where[i][2]) // B + b for i, b in picks for j in range(P)])
+    rq_ef_o = np.zeros(out_blocks.size * B, np.float32)
+    for step in range(2):
+        synth.fill_model(g, tensors, std=1e-3, seed=synth.seed_for("llama7p5b", "grad", step=step),
+                         heavy_tails=True)
+        Z().zq_quantize_ef_int4(g, None, B, 0.0, 1.0, codes, scales)
+        rqc.fill_(0x88)
+        rqs.fill_(float("nan"))
+        Z().zq_dequant_reduce_batched(table, P, B, 1.0, rq_beta_e=0.9, rq_beta_r=1.0)
+        torch.cuda.synchronize()
+        what = f"7.5B per-tensor reduce step {step}"
+        assert not bool(((rqc & 0x0F) == 8).any() | ((rqc >> 4) == 8).any()), what + ": codes unwritten"
+        assert not bool(torch.isnan(rqs).any()), what + ": scales unwritten"
+        # oracle: the 8 input blocks of every tracked output block, in order
+        c0, s0 = O.quantize_ef_int4(gather_blocks(g, in_blocks, B), None, B, 0.0, 1.0)
+        k = out_blocks.size
+        cj = [np.concatenate([c0[(q * P + j) * B // 2:(q * P + j + 1) * B // 2] for q in range(k)])
+              for j in range(P)]
+        sj = [np.array([s0[q * P + j] for q in range(k)], np.float32) for j in range(P)]
+        _, rc_o, rs_o = O.dequant_reduce(cj, sj, k * B, B, 1.0, want_out=False, requant=True,
+                                         rq_ef=rq_ef_o, rq_beta_e=0.9, rq_beta_r=1.0)
+        assert_bits_equal(int4_block_bytes(rqc, out_blocks, B), rc_o, what + " requant codes")
+        assert_bits_equal(to_host(rqs)[out_blocks], rs_o, what + " requant scales")
+        assert_bits_equal(gather_blocks(rq_ef, out_blocks, B), rq_ef_o, what + " requant ef")

@@ -55,9 +55,18 @@ def test_traffic_is_read_only_for_the_profiled_source(tmp_path, monkeypatch):
 
 
 def test_traffic_summary_records_hash_and_bytes():
-    text = open(os.path.join(ROOT, "profiles", "efq_fp32_b128_counters.md")).read()
-    assert re.search(r"source_sha256[^:\n]*:\s*[0-9a-f]{64}", text)
-    assert re.search(r"hbm_bytes_per_launch:\s*[0-9]+", text)
+    for tag in bench.KERNEL_SOURCES:
+        text = open(os.path.join(ROOT, "profiles", f"{tag}_counters.md")).read()
+        assert re.search(r"source_sha256[^:\n]*:\s*[0-9a-f]{64}", text), tag
+        assert re.search(r"hbm_bytes_per_launch:\s*[0-9]+", text), tag
+
+
+def test_reduce_traffic_is_current_and_near_algorithmic():
+    n1 = 7547949056 // 8
+    alg = 8 * (n1 // 2 + 4 * (n1 // 128)) + n1 // 2 + 4 * (n1 // 128)
+    got = bench.measured_traffic("dequant_reduce_requant_p8_b128_7.5B", alg)
+    assert got is not None, "the reduce's counter summary no longer matches its source"
+    assert 1.0 <= got / alg < 1.1
 
 
 def test_pages_context_counts_bytes_with_the_library_helpers():
