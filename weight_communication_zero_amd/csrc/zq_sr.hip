@@ -96,37 +96,38 @@ __device__ __forceinline__ void sr_tile(uint16_t* __restrict__ dst, uint16_t* __
     }
 }
 
-template <int PHASE, bool ZERO, bool MASK>
+// Full tiles and the ragged last tile in one launch: the tile past the last
+// full one (when n is not a multiple of the tile) takes the masked path.
+template <int PHASE, bool ZERO>
 __global__ __launch_bounds__(kBlockThreads) void sr_kernel(uint16_t* __restrict__ dst,
                                                            uint16_t* __restrict__ src, size_t n,
                                                            uint32_t k0, uint32_t k1,
                                                            uint64_t cbase8) {
-    if constexpr (MASK) {
-        sr_tile<PHASE, ZERO, true>(dst, src, n, k0, k1, cbase8, n / kSrTile);
-    } else {
-        const size_t nfull = n / kSrTile;
-        for (size_t t = stream_wave_id<kGeomStream.threads>(); t < nfull; t += wave_count())
+    const size_t nfull = n / kSrTile;
+    const size_t ntiles = nfull + (n % kSrTile ? 1 : 0);
+    for (size_t t = stream_wave_id<kGeomStream.threads>(); t < ntiles; t += wave_count()) {
+        if (t < nfull)
             sr_tile<PHASE, ZERO, false>(dst, src, n, k0, k1, cbase8, t);
+        else
+            sr_tile<PHASE, ZERO, true>(dst, src, n, k0, k1, cbase8, t);
     }
 }
 
-template <int PHASE, bool MASK>
+template <int PHASE>
 const void* sr_fn(bool zero) {
-    return zero ? (const void*)&sr_kernel<PHASE, true, MASK>
-                : (const void*)&sr_kernel<PHASE, false, MASK>;
+    return zero ? (const void*)&sr_kernel<PHASE, true> : (const void*)&sr_kernel<PHASE, false>;
 }
 
-template <bool MASK>
 const void* sr_pick(uint64_t counter_base, bool zero) {
     switch (counter_base & 7u) {
-        case 0: return sr_fn<0, MASK>(zero);
-        case 1: return sr_fn<1, MASK>(zero);
-        case 2: return sr_fn<2, MASK>(zero);
-        case 3: return sr_fn<3, MASK>(zero);
-        case 4: return sr_fn<4, MASK>(zero);
-        case 5: return sr_fn<5, MASK>(zero);
-        case 6: return sr_fn<6, MASK>(zero);
-        default: return sr_fn<7, MASK>(zero);
+        case 0: return sr_fn<0>(zero);
+        case 1: return sr_fn<1>(zero);
+        case 2: return sr_fn<2>(zero);
+        case 3: return sr_fn<3>(zero);
+        case 4: return sr_fn<4>(zero);
+        case 5: return sr_fn<5>(zero);
+        case 6: return sr_fn<6>(zero);
+        default: return sr_fn<7>(zero);
     }
 }
 
@@ -260,17 +261,10 @@ hipError_t launch_sr_accumulate(uint16_t* dst, uint16_t* src, size_t n, uint64_t
                                 uint64_t counter_base, bool zero_src, hipStream_t stream) {
     uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
     uint64_t cbase8 = counter_base >> 3;
-    const size_t nfull = n / kSrTile;
+    const size_t ntiles = (n + kSrTile - 1) / kSrTile;
     void* args[] = {(void*)&dst, (void*)&src, (void*)&n, (void*)&k0, (void*)&k1, (void*)&cbase8};
-    hipError_t e = hipSuccess;
-    if (nfull)
-        e = hipLaunchKernel(sr_pick<false>(counter_base, zero_src),
-                            grid_for_tiles(nfull, kGeomStream), dim3(kGeomStream.threads), args, 0,
-                            stream);
-    if (e == hipSuccess && n % kSrTile)
-        e = hipLaunchKernel(sr_pick<true>(counter_base, zero_src), dim3(1), dim3(kWave), args, 0,
-                            stream);
-    return e;
+    return hipLaunchKernel(sr_pick(counter_base, zero_src), grid_for_tiles(ntiles, kGeomStream),
+                           dim3(kGeomStream.threads), args, 0, stream);
 }
 
 hipError_t launch_sr_accumulate_batched(const SrSegment* segs, uint32_t n_seg, bool zero_src,
