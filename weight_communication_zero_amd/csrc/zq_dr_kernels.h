@@ -652,39 +652,34 @@ __device__ __forceinline__ void dr_tile(const PV& p, size_t tile) {
 }
 
 // PMAX: the kernel serves every P <= PMAX; only PMAX pointer pairs stay
-// live, so the common P = 4 / 8 cases keep their pointers in SGPRs.  Full
-// tiles only; the ragged last tile is a second one-wave launch (MASK).
-template <int B, int PMAX, bool OUT, bool RQ, bool EF, bool MASK>
+// live, so the common P = 4 / 8 cases keep their pointers in SGPRs.  The
+// loop runs the full tiles without bounds checks; the ragged last tile (when
+// n is not a multiple of the tile) goes to the one wave whose loop stops
+// exactly at it, in the same launch.
+template <int B, int PMAX, bool OUT, bool RQ, bool EF>
 __global__ __launch_bounds__(kBlockThreads) void dr_kernel(DrParams p) {
     using G = DrGeomOf<B, RQ, EF>;
-    if constexpr (MASK) {
-        dr_tile<B, PMAX, OUT, RQ, EF, true>(p, p.n / G::TILE);
-    } else {
-        const size_t nfull = p.n / G::TILE;
-        // Plain dispatch order: the XCD-contiguous order of the streaming
-        // kernels measured slower here (P peer streams per XCD run).
-        for (size_t t = wave_id(); t < nfull; t += wave_count())
-            dr_tile<B, PMAX, OUT, RQ, EF, false>(p, t);
-    }
+    const size_t nfull = p.n / G::TILE;
+    // Plain dispatch order: the XCD-contiguous order of the streaming
+    // kernels measured slower here (P peer streams per XCD run).
+    size_t t = wave_id();
+    for (; t < nfull; t += wave_count())
+        dr_tile<B, PMAX, OUT, RQ, EF, false>(p, t);
+    if (t == nfull && p.n % G::TILE)
+        dr_tile<B, PMAX, OUT, RQ, EF, true>(p, t);
 }
 
 template <int B, int PMAX, bool OUT, bool RQ, bool EF>
 hipError_t launch_b(const DrParams& p, hipStream_t stream) {
     using G = DrGeomOf<B, RQ, EF>;
-    const size_t nfull = p.n / G::TILE;
+    const size_t ntiles = (p.n + G::TILE - 1) / G::TILE;
     DrParams arg = p;
     void* args[] = {(void*)&arg};
     // Requant without EF keeps a persistent grid; with EF (two more fp32
     // streams) one tile per wave keeps more bytes in flight and is faster.
     const Geometry geom = (RQ && !EF) ? kGeomReduceRequant : kGeomReduce;
-    hipError_t e = hipSuccess;
-    if (nfull)
-        e = hipLaunchKernel((const void*)&dr_kernel<B, PMAX, OUT, RQ, EF, false>,
-                            grid_for_tiles(nfull, geom), dim3(geom.threads), args, 0, stream);
-    if (e == hipSuccess && p.n % G::TILE)
-        e = hipLaunchKernel((const void*)&dr_kernel<B, PMAX, OUT, RQ, EF, true>, dim3(1),
-                            dim3(kWave), args, 0, stream);
-    return e;
+    return hipLaunchKernel((const void*)&dr_kernel<B, PMAX, OUT, RQ, EF>,
+                           grid_for_tiles(ntiles, geom), dim3(geom.threads), args, 0, stream);
 }
 
 template <int B, int PMAX>
@@ -716,10 +711,10 @@ hipError_t launch_peers(const DrParams& p, hipStream_t st) {
 // Batched segments: the per-parameter receive side ("Merge LoCo with Zero++",
 // review thread: the LoCo path reduces parameter by parameter, each with its
 // own requant error-feedback buffer).  A launch takes up to kDrSegs segments
-// (the table rides in the kernel arguments); as in the batched EF quantize,
-// the first pass runs the full tiles of all segments, a wave finding its
-// segment by binary search over the cumulative tile counts, and the second
-// pass runs every segment's ragged last tile.
+// (the table rides in the kernel arguments) and runs all of their tiles:
+// first the full ones, a wave finding its segment by binary search over the
+// cumulative full-tile counts, then the ragged last tiles, the k-th of which
+// belongs to segment tail_seg[k].
 #ifndef ZQ_DR_SEGS
 #define ZQ_DR_SEGS 48
 #endif
@@ -727,12 +722,15 @@ constexpr int kDrSegs = ZQ_DR_SEGS;
 
 struct DrBatch {
     DrSegment seg[kDrSegs];
-    uint32_t tile_end[kDrSegs];  // cumulative tiles through segment s
+    uint32_t tile_end[kDrSegs];  // cumulative full tiles through segment s
+    uint8_t tail_seg[kDrSegs];   // segment of the k-th ragged last tile
     uint32_t nseg;
-    uint32_t total;
+    uint32_t full;   // full tiles of all segments
+    uint32_t total;  // full + ragged tiles
     uint32_t P;
     float alpha, rq_beta_e, rq_beta_r;
 };
+static_assert(kDrSegs <= 256, "tail_seg holds 8-bit segment indices");
 
 // A segment seen through the reduce tile's parameter interface.
 struct DrSegView {
@@ -764,19 +762,25 @@ __device__ __forceinline__ uint32_t find_dr_segment(const DrBatch& b, uint32_t t
     return lo;
 }
 
-template <int B, int PMAX, bool OUT, bool RQ, bool EF, bool MASK>
+template <int B, int PMAX, bool OUT, bool RQ, bool EF>
 __global__ __launch_bounds__(kBlockThreads) void dr_batched_kernel(DrBatch b) {
     using G = DrGeomOf<B, RQ, EF>;
-    for (size_t ts = wave_id(); ts < b.total; ts += wave_count()) {
+    size_t ts = wave_id();
+    for (; ts < b.full; ts += wave_count()) {
         const uint32_t t = (uint32_t)ts;
         const uint32_t s = find_dr_segment(b, t);
         const DrSegment& g = b.seg[s];
         const DrSegView v = {g.codes,    g.scales,    g.codes_stride, g.scales_stride, b.P,
                              g.n,        b.alpha,     g.out,          g.rq_codes,      g.rq_scales,
                              g.rq_ef,    b.rq_beta_e, b.rq_beta_r};
-        // full tiles: the local index within the segment; tails: its last tile
-        const size_t local = MASK ? g.n / G::TILE : t - (s ? b.tile_end[s - 1] : 0u);
-        dr_tile<B, PMAX, OUT, RQ, EF, MASK>(v, local);
+        dr_tile<B, PMAX, OUT, RQ, EF, false>(v, t - (s ? b.tile_end[s - 1] : 0u));
+    }
+    for (; ts < b.total; ts += wave_count()) {
+        const DrSegment& g = b.seg[b.tail_seg[ts - b.full]];
+        const DrSegView v = {g.codes,    g.scales,    g.codes_stride, g.scales_stride, b.P,
+                             g.n,        b.alpha,     g.out,          g.rq_codes,      g.rq_scales,
+                             g.rq_ef,    b.rq_beta_e, b.rq_beta_r};
+        dr_tile<B, PMAX, OUT, RQ, EF, true>(v, g.n / G::TILE);
     }
 }
 
@@ -786,41 +790,41 @@ hipError_t launch_batched_b(const DrSegment* segs, uint32_t n_seg, const DrBatch
     using G = DrGeomOf<B, RQ, EF>;
     static_assert(G::TILE >= 512, "2^40-element segments need tiles of >= 512");
     const Geometry geom = (RQ && !EF) ? kGeomReduceRequant : kGeomReduce;
-    for (int pass = 0; pass < 2; ++pass) {  // 0: full tiles, 1: ragged last tiles
-        uint32_t i = 0;
-        while (i < n_seg) {
-            DrBatch bt = {};
-            bt.P = a.P;
-            bt.alpha = a.alpha;
-            bt.rq_beta_e = a.rq_beta_e;
-            bt.rq_beta_r = a.rq_beta_r;
-            uint64_t tiles = 0;
-            // A launch takes segments while its tile count (32-bit in the
-            // kernel's table) stays below 2^32.
-            while (i < n_seg && bt.nseg < (uint32_t)kDrSegs) {
-                const DrSegment& g = segs[i];
-                const uint64_t t = pass == 0 ? g.n / G::TILE : (g.n % G::TILE ? 1 : 0);
-                if (tiles + t > UINT32_MAX)
-                    break;  // the next launch starts with this segment
-                ++i;
-                if (t == 0)
-                    continue;
-                bt.seg[bt.nseg] = g;
-                tiles += t;
-                bt.tile_end[bt.nseg++] = (uint32_t)tiles;
-            }
-            if (bt.nseg == 0)
+    uint32_t i = 0;
+    while (i < n_seg) {
+        DrBatch bt = {};
+        bt.P = a.P;
+        bt.alpha = a.alpha;
+        bt.rq_beta_e = a.rq_beta_e;
+        bt.rq_beta_r = a.rq_beta_r;
+        uint64_t full = 0, tails = 0;
+        // A launch takes segments while its tile count (32-bit in the
+        // kernel's table) stays below 2^32.
+        while (i < n_seg && bt.nseg < (uint32_t)kDrSegs) {
+            const DrSegment& g = segs[i];
+            const uint64_t f = g.n / G::TILE, r = g.n % G::TILE ? 1 : 0;
+            if (full + tails + f + r > UINT32_MAX)
+                break;  // the next launch starts with this segment
+            ++i;
+            if (f + r == 0)
                 continue;
-            bt.total = (uint32_t)tiles;
-            void* args[] = {(void*)&bt};
-            const void* fn = pass == 0 ? (const void*)&dr_batched_kernel<B, PMAX, OUT, RQ, EF, false>
-                                       : (const void*)&dr_batched_kernel<B, PMAX, OUT, RQ, EF, true>;
-            const Geometry g = pass == 0 ? geom : Geometry{kWave, 1u << 22};
-            const hipError_t e = hipLaunchKernel(fn, grid_for_tiles(tiles, g), dim3(g.threads),
-                                                 args, 0, stream);
-            if (e != hipSuccess)
-                return e;
+            if (r)
+                bt.tail_seg[tails++] = (uint8_t)bt.nseg;
+            bt.seg[bt.nseg] = g;
+            full += f;
+            bt.tile_end[bt.nseg++] = (uint32_t)full;
         }
+        if (bt.nseg == 0)
+            continue;
+        const uint64_t tiles = full + tails;
+        bt.full = (uint32_t)full;
+        bt.total = (uint32_t)tiles;
+        void* args[] = {(void*)&bt};
+        const hipError_t e =
+            hipLaunchKernel((const void*)&dr_batched_kernel<B, PMAX, OUT, RQ, EF>,
+                            grid_for_tiles(tiles, geom), dim3(geom.threads), args, 0, stream);
+        if (e != hipSuccess)
+            return e;
     }
     return hipSuccess;
 }

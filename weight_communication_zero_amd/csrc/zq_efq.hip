@@ -206,43 +206,38 @@ __device__ __forceinline__ void efq_tile(const void* __restrict__ gv, float* __r
     }
 }
 
-// Full tiles only (no bounds checks in the hot loop); the ragged last tile,
-// if any, is a second one-wave launch of the masked variant.
-template <bool BF16, bool EF, int B, bool MASK>
+// Full tiles without bounds checks; the ragged last tile (when n is not a
+// multiple of the tile) goes, in the same launch, to the one wave whose loop
+// stops exactly at it.  The two paths run one after the other, so their
+// registers are not live at once.
+template <bool BF16, bool EF, int B>
 __global__ __launch_bounds__(kBlockThreads) void efq_kernel(const void* __restrict__ g,
                                                             float* __restrict__ ef, size_t n,
                                                             float beta_e, float beta_r,
                                                             uint8_t* __restrict__ codes,
                                                             float* __restrict__ scales) {
     using G = EfqGeom<B>;
-    if constexpr (MASK) {
-        efq_tile<BF16, EF, B, true>(g, ef, n, beta_e, beta_r, codes, scales, n / G::TILE);
-    } else {
-        const size_t nfull = n / G::TILE;
-        for (size_t t = stream_wave_id<kGeomStream.threads>(); t < nfull; t += wave_count())
-            efq_tile<BF16, EF, B, false>(g, ef, n, beta_e, beta_r, codes, scales, t);
-    }
+    const size_t nfull = n / G::TILE;
+    size_t t = stream_wave_id<kGeomStream.threads>();
+    for (; t < nfull; t += wave_count())
+        efq_tile<BF16, EF, B, false>(g, ef, n, beta_e, beta_r, codes, scales, t);
+    if (t == nfull && n % G::TILE)
+        efq_tile<BF16, EF, B, true>(g, ef, n, beta_e, beta_r, codes, scales, t);
 }
 
 template <bool BF16, bool EF, int B>
 hipError_t launch_b(const void* g, float* ef, size_t n, float beta_e, float beta_r,
                     uint8_t* codes, float* scales, hipStream_t stream) {
     using G = EfqGeom<B>;
-    const size_t nfull = n / G::TILE;
+    const size_t ntiles = (n + G::TILE - 1) / G::TILE;
     void* args[] = {(void*)&g, (void*)&ef, (void*)&n, (void*)&beta_e, (void*)&beta_r,
                     (void*)&codes, (void*)&scales};
-    hipError_t e = hipSuccess;
-    if (nfull)
-        e = hipLaunchKernel((const void*)&efq_kernel<BF16, EF, B, false>,
-                            grid_for_tiles(nfull, kGeomStream), dim3(kGeomStream.threads), args, 0,
-                            stream);
-    if (e == hipSuccess && n % G::TILE)
-        e = hipLaunchKernel((const void*)&efq_kernel<BF16, EF, B, true>, dim3(1), dim3(kWave),
-                            args, 0, stream);
-    return e;
+    return hipLaunchKernel((const void*)&efq_kernel<BF16, EF, B>,
+                           grid_for_tiles(ntiles, kGeomStream), dim3(kGeomStream.threads), args, 0,
+                           stream);
 }
 
-template <bool BF16, bool EF, int B, bool MASK>
+template <bool BF16, bool EF, int B>
 __global__ __launch_bounds__(kBlockThreads) void efq_perm_kernel(const void* __restrict__ g,
                                                                  float* __restrict__ ef, size_t n,
                                                                  float beta_e, float beta_r,
@@ -250,35 +245,27 @@ __global__ __launch_bounds__(kBlockThreads) void efq_perm_kernel(const void* __r
                                                                  float* __restrict__ scales,
                                                                  PartPerm perm) {
     using G = EfqGeom<B>;
-    if constexpr (MASK) {
-        const size_t t = n / G::TILE;
+    const size_t nfull = n / G::TILE;
+    size_t t = stream_wave_id<kGeomStream.threads>();
+    for (; t < nfull; t += wave_count())
+        efq_tile<BF16, EF, B, false>(g, ef, n, beta_e, beta_r, codes, scales, t,
+                                     perm_map(perm, t * G::TILE));
+    if (t == nfull && n % G::TILE)
         efq_tile<BF16, EF, B, true>(g, ef, n, beta_e, beta_r, codes, scales, t,
                                     perm_map(perm, t * G::TILE));
-    } else {
-        const size_t nfull = n / G::TILE;
-        for (size_t t = stream_wave_id<kGeomStream.threads>(); t < nfull; t += wave_count())
-            efq_tile<BF16, EF, B, false>(g, ef, n, beta_e, beta_r, codes, scales, t,
-                                         perm_map(perm, t * G::TILE));
-    }
 }
 
 template <bool BF16, bool EF, int B>
 hipError_t launch_perm_b(const void* g, float* ef, size_t n, float beta_e, float beta_r,
                          uint8_t* codes, float* scales, const PartPerm& perm, hipStream_t stream) {
     using G = EfqGeom<B>;
-    const size_t nfull = n / G::TILE;
+    const size_t ntiles = (n + G::TILE - 1) / G::TILE;
     PartPerm arg = perm;
     void* args[] = {(void*)&g, (void*)&ef, (void*)&n, (void*)&beta_e, (void*)&beta_r,
                     (void*)&codes, (void*)&scales, (void*)&arg};
-    hipError_t e = hipSuccess;
-    if (nfull)
-        e = hipLaunchKernel((const void*)&efq_perm_kernel<BF16, EF, B, false>,
-                            grid_for_tiles(nfull, kGeomStream), dim3(kGeomStream.threads), args, 0,
-                            stream);
-    if (e == hipSuccess && n % G::TILE)
-        e = hipLaunchKernel((const void*)&efq_perm_kernel<BF16, EF, B, true>, dim3(1),
-                            dim3(kWave), args, 0, stream);
-    return e;
+    return hipLaunchKernel((const void*)&efq_perm_kernel<BF16, EF, B>,
+                           grid_for_tiles(ntiles, kGeomStream), dim3(kGeomStream.threads), args, 0,
+                           stream);
 }
 
 template <bool BF16, bool EF>
@@ -297,12 +284,12 @@ hipError_t launch_perm_t(const void* g, float* ef, size_t n, uint32_t block, flo
     }
 }
 
-// Batched segments.  The main launch runs the full tiles of up to kEfqSegs
-// segments; a second launch runs every segment's ragged last tile (masked),
-// one wave each.  A wave finds its segment by binary search over the
-// cumulative tile counts in the kernel arguments (seven scalar loads).
-// 80 segments (3.5 KB of kernel arguments) take the 7.5B model's 327 tensors
-// in 5 launches instead of 11.
+// Batched segments.  One launch runs every tile of up to kEfqSegs segments:
+// first all full tiles (a wave finds its segment by binary search over the
+// cumulative full-tile counts in the kernel arguments, seven scalar loads),
+// then the ragged last tiles, the k-th of which belongs to segment
+// tail_seg[k].  80 segments (3.6 KB of kernel arguments) take the 7.5B
+// model's 327 tensors in 5 launches.
 #ifndef ZQ_EFQ_SEGS
 #define ZQ_EFQ_SEGS 80
 #endif
@@ -310,11 +297,14 @@ constexpr int kEfqSegs = ZQ_EFQ_SEGS;
 
 struct EfqBatch {
     EfqSegment seg[kEfqSegs];
-    uint32_t tile_end[kEfqSegs];  // cumulative tiles through segment s
+    uint32_t tile_end[kEfqSegs];  // cumulative full tiles through segment s
+    uint8_t tail_seg[kEfqSegs];   // segment of the k-th ragged last tile
     uint32_t nseg;
-    uint32_t total;
+    uint32_t full;   // full tiles of all segments
+    uint32_t total;  // full + ragged tiles
     float beta_e, beta_r;
 };
+static_assert(kEfqSegs <= 256, "tail_seg holds 8-bit segment indices");
 
 __device__ __forceinline__ uint32_t find_segment(const EfqBatch& b, uint32_t t) {
     uint32_t lo = 0, hi = b.nseg - 1;  // first s with t < tile_end[s]
@@ -328,16 +318,21 @@ __device__ __forceinline__ uint32_t find_segment(const EfqBatch& b, uint32_t t) 
     return lo;
 }
 
-template <bool BF16, bool EF, int B, bool MASK>
+template <bool BF16, bool EF, int B>
 __global__ __launch_bounds__(kBlockThreads) void efq_batched_kernel(EfqBatch b) {
     using G = EfqGeom<B>;
-    for (size_t ts = stream_wave_id<kGeomStream.threads>(); ts < b.total; ts += wave_count()) {
+    size_t ts = stream_wave_id<kGeomStream.threads>();
+    for (; ts < b.full; ts += wave_count()) {
         const uint32_t t = (uint32_t)ts;
         const uint32_t s = find_segment(b, t);
         const EfqSegment& g = b.seg[s];
-        // full tiles: local index within the segment; tails: the segment's last tile
-        const size_t local = MASK ? g.n / G::TILE : t - (s ? b.tile_end[s - 1] : 0u);
-        efq_tile<BF16, EF, B, MASK>(g.g, g.ef, g.n, b.beta_e, b.beta_r, g.codes, g.scales, local);
+        const size_t local = t - (s ? b.tile_end[s - 1] : 0u);
+        efq_tile<BF16, EF, B, false>(g.g, g.ef, g.n, b.beta_e, b.beta_r, g.codes, g.scales, local);
+    }
+    for (; ts < b.total; ts += wave_count()) {
+        const EfqSegment& g = b.seg[b.tail_seg[ts - b.full]];
+        efq_tile<BF16, EF, B, true>(g.g, g.ef, g.n, b.beta_e, b.beta_r, g.codes, g.scales,
+                                    g.n / G::TILE);
     }
 }
 
@@ -345,40 +340,42 @@ template <bool BF16, bool EF, int B>
 hipError_t launch_batched_b(const EfqSegment* segs, uint32_t n_seg, float be, float br,
                             hipStream_t stream) {
     using G = EfqGeom<B>;
-    for (int pass = 0; pass < 2; ++pass) {  // 0: full tiles, 1: ragged last tiles
-        uint32_t i = 0;
-        while (i < n_seg) {
-            EfqBatch bt = {};
-            bt.beta_e = be;
-            bt.beta_r = br;
-            uint64_t tiles = 0;
-            // A launch takes segments while its tile count (32-bit in the
-            // kernel's table) stays below 2^32; one segment (at most 2^40
-            // elements) has fewer than 2^32 tiles.
-            static_assert(G::TILE >= 512, "2^40-element segments need tiles of >= 512");
-            while (i < n_seg && bt.nseg < (uint32_t)kEfqSegs) {
-                const EfqSegment& g = segs[i];
-                const uint64_t t = pass == 0 ? g.n / G::TILE : (g.n % G::TILE ? 1 : 0);
-                if (tiles + t > UINT32_MAX)
-                    break;  // the next launch starts with this segment
-                ++i;
-                if (t == 0)
-                    continue;
-                bt.seg[bt.nseg] = g;
-                tiles += t;
-                bt.tile_end[bt.nseg++] = (uint32_t)tiles;
-            }
-            if (bt.nseg == 0)
+    uint32_t i = 0;
+    while (i < n_seg) {
+        EfqBatch bt = {};
+        bt.beta_e = be;
+        bt.beta_r = br;
+        uint64_t full = 0, tails = 0;
+        // A launch takes segments while its tile count (32-bit in the kernel's
+        // table) stays below 2^32; one segment (at most 2^40 elements) has
+        // fewer than 2^32 tiles.
+        static_assert(G::TILE >= 512, "2^40-element segments need tiles of >= 512");
+        while (i < n_seg && bt.nseg < (uint32_t)kEfqSegs) {
+            const EfqSegment& g = segs[i];
+            const uint64_t f = g.n / G::TILE, r = g.n % G::TILE ? 1 : 0;
+            if (full + tails + f + r > UINT32_MAX)
+                break;  // the next launch starts with this segment
+            ++i;
+            if (f + r == 0)
                 continue;
-            bt.total = (uint32_t)tiles;
-            void* args[] = {(void*)&bt};
-            const void* fn = pass == 0 ? (const void*)&efq_batched_kernel<BF16, EF, B, false>
-                                       : (const void*)&efq_batched_kernel<BF16, EF, B, true>;
-            const hipError_t e = hipLaunchKernel(fn, grid_for_tiles(tiles, kGeomStream),
-                                                 dim3(kGeomStream.threads), args, 0, stream);
-            if (e != hipSuccess)
-                return e;
+            if (r)
+                bt.tail_seg[tails++] = (uint8_t)bt.nseg;
+            bt.seg[bt.nseg] = g;
+            full += f;
+            bt.tile_end[bt.nseg++] = (uint32_t)full;
         }
+        if (bt.nseg == 0)
+            continue;
+        const uint64_t tiles = full + tails;
+        bt.full = (uint32_t)full;
+        bt.total = (uint32_t)tiles;
+        void* args[] = {(void*)&bt};
+        const hipError_t e =
+            hipLaunchKernel((const void*)&efq_batched_kernel<BF16, EF, B>,
+                            grid_for_tiles(tiles, kGeomStream), dim3(kGeomStream.threads), args, 0,
+                            stream);
+        if (e != hipSuccess)
+            return e;
     }
     return hipSuccess;
 }

@@ -143,18 +143,20 @@ __device__ __forceinline__ void q8_tile(const void* __restrict__ wv, size_t n,
     }
 }
 
-template <bool BF16, int B, bool MASK>
+// Full tiles without bounds checks; the ragged last tile goes, in the same
+// launch, to the one wave whose loop stops exactly at it (the two paths are
+// never live at once, so the masked one costs the loop no registers).
+template <bool BF16, int B>
 __global__ __launch_bounds__(kBlockThreads) void q8_kernel(const void* __restrict__ w, size_t n,
                                                            int8_t* __restrict__ codes,
                                                            float* __restrict__ scales) {
     using G = Q8Geom<B>;
-    if constexpr (MASK) {
-        q8_tile<BF16, B, true>(w, n, codes, scales, n / G::TILE);
-    } else {
-        const size_t nfull = n / G::TILE;
-        for (size_t t = stream_wave_id<kGeomStream.threads>(); t < nfull; t += wave_count())
-            q8_tile<BF16, B, false>(w, n, codes, scales, t);
-    }
+    const size_t nfull = n / G::TILE;
+    size_t t = stream_wave_id<kGeomStream.threads>();
+    for (; t < nfull; t += wave_count())
+        q8_tile<BF16, B, false>(w, n, codes, scales, t);
+    if (t == nfull && n % G::TILE)
+        q8_tile<BF16, B, true>(w, n, codes, scales, t);
 }
 
 // Dequantize: lane l of sub-vector u owns 8 codes (one 8-byte load) that lie
@@ -235,34 +237,26 @@ __device__ __forceinline__ void dq8_tile(const int8_t* __restrict__ codes,
     }
 }
 
-template <bool BF16OUT, bool MASK>
+template <bool BF16OUT>
 __global__ __launch_bounds__(kBlockThreads) void dq8_kernel(const int8_t* __restrict__ codes,
                                                             const float* __restrict__ scales,
                                                             size_t n, uint32_t log2b,
                                                             void* __restrict__ out) {
-    if constexpr (MASK) {
-        dq8_tile<BF16OUT, true>(codes, scales, n, log2b, out, n / kDqTile);
-    } else {
-        const size_t nfull = n / kDqTile;
-        for (size_t t = stream_wave_id<kGeomStream.threads>(); t < nfull; t += wave_count())
-            dq8_tile<BF16OUT, false>(codes, scales, n, log2b, out, t);
-    }
+    const size_t nfull = n / kDqTile;
+    size_t t = stream_wave_id<kGeomStream.threads>();
+    for (; t < nfull; t += wave_count())
+        dq8_tile<BF16OUT, false>(codes, scales, n, log2b, out, t);
+    if (t == nfull && n % kDqTile)
+        dq8_tile<BF16OUT, true>(codes, scales, n, log2b, out, t);
 }
 
 template <bool BF16, int B>
 hipError_t launch_q8_b(const void* w, size_t n, int8_t* codes, float* scales, hipStream_t st) {
     using G = Q8Geom<B>;
-    const size_t nfull = n / G::TILE;
+    const size_t ntiles = (n + G::TILE - 1) / G::TILE;
     void* args[] = {(void*)&w, (void*)&n, (void*)&codes, (void*)&scales};
-    hipError_t e = hipSuccess;
-    if (nfull)
-        e = hipLaunchKernel((const void*)&q8_kernel<BF16, B, false>,
-                            grid_for_tiles(nfull, kGeomStream), dim3(kGeomStream.threads), args, 0,
-                            st);
-    if (e == hipSuccess && n % G::TILE)
-        e = hipLaunchKernel((const void*)&q8_kernel<BF16, B, true>, dim3(1), dim3(kWave), args, 0,
-                            st);
-    return e;
+    return hipLaunchKernel((const void*)&q8_kernel<BF16, B>, grid_for_tiles(ntiles, kGeomStream),
+                           dim3(kGeomStream.threads), args, 0, st);
 }
 
 template <bool BF16>
@@ -294,19 +288,11 @@ hipError_t launch_dequant_int8(const int8_t* codes, const float* scales, size_t 
     uint32_t log2b = 0;
     while ((1u << log2b) < block)
         ++log2b;
-    const size_t nfull = n / kDqTile;
+    const size_t ntiles = (n + kDqTile - 1) / kDqTile;
     void* args[] = {(void*)&codes, (void*)&scales, (void*)&n, (void*)&log2b, (void*)&out};
-    const void* full = out_bf16 ? (const void*)&dq8_kernel<true, false>
-                                : (const void*)&dq8_kernel<false, false>;
-    const void* tail = out_bf16 ? (const void*)&dq8_kernel<true, true>
-                                : (const void*)&dq8_kernel<false, true>;
-    hipError_t e = hipSuccess;
-    if (nfull)
-        e = hipLaunchKernel(full, grid_for_tiles(nfull, kGeomStream), dim3(kGeomStream.threads),
-                            args, 0, stream);
-    if (e == hipSuccess && n % kDqTile)
-        e = hipLaunchKernel(tail, dim3(1), dim3(kWave), args, 0, stream);
-    return e;
+    const void* fn = out_bf16 ? (const void*)&dq8_kernel<true> : (const void*)&dq8_kernel<false>;
+    return hipLaunchKernel(fn, grid_for_tiles(ntiles, kGeomStream), dim3(kGeomStream.threads), args,
+                           0, stream);
 }
 
 }  // namespace zq
