@@ -119,12 +119,28 @@ __device__ __forceinline__ void nib16(uint32_t w, float (&f)[V]) {
 // recovers rne(y) exactly -- as +0 where rintf gives -0, which the integer
 // code does not see.  The caller guarantees a finite block scale, so
 // |y| <= qmax (1 + 2^-22) unless `redo` is set anyway.
+#ifndef ZQ_DR_FMA_ROUND
+#define ZQ_DR_FMA_ROUND 1
+#endif
 template <int QMAX>
 __device__ __forceinline__ float code_fast_rne(float x, const BlockScale& b, bool& redo) {
-    const float y = x * b.inv;
-    const float k = (y + 0x1.8p23f) - 0x1.8p23f;
-    redo |= __builtin_fabsf(y - k) > tie_band<QMAX>();
-    return k;
+    if constexpr (ZQ_DR_FMA_ROUND) {
+        // The same code from the exact product z = x rcp(s): fma(x, rcp(s),
+        // 1.5 2^23) rounds z itself onto the integers, and fma(x, rcp(s), -k)
+        // is z - k to 2^-25.  With |z - x / s| < 2^-20 and fl(x / s) within
+        // 2^-22 of x / s, a distance of at least 2^-17 - 2^-25 from every
+        // half-integer puts z and fl(x / s) on the same side of it, so outside
+        // the tie band k = rne(fl(x / s)).  Three dual-issue FMA/add
+        // instructions instead of four.
+        const float k = __builtin_fmaf(x, b.inv, 0x1.8p23f) - 0x1.8p23f;
+        redo |= __builtin_fabsf(__builtin_fmaf(x, b.inv, -k)) > tie_band<QMAX>();
+        return k;
+    } else {
+        const float y = x * b.inv;
+        const float k = (y + 0x1.8p23f) - 0x1.8p23f;
+        redo |= __builtin_fabsf(y - k) > tie_band<QMAX>();
+        return k;
+    }
 }
 
 // Two's-complement nibbles of V (4 or 8) integer-valued floats in [-7, 7],
@@ -417,29 +433,45 @@ __device__ __forceinline__ void rq_compensate(const PV& p, size_t base, float (&
     }
 }
 
+// Running absmax of one lane's requant inputs, as float bits.  gfx950's
+// v_maximum3_f32 takes two |c| per instruction (abs is an operand modifier)
+// and, as IEEE 754-2019 maximum, returns NaN when any input is NaN, so a NaN
+// sum still gives a non-finite block scale, as the integer maximum over the
+// magnitude bits does.  On non-negative floats both orders agree.
+#ifndef ZQ_DR_FMAXIMUM
+#define ZQ_DR_FMAXIMUM 1
+#endif
+template <int V>
+__device__ __forceinline__ uint32_t lane_absmax(const float (&c)[V], uint32_t m) {
+    if constexpr (ZQ_DR_FMAXIMUM) {
+        float f = bitsf(m);
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+            f = __builtin_elementwise_maximum(f, __builtin_fabsf(c[j]));
+        return fbits(f);
+    } else {
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+            m = max(m, absbits(c[j]));
+        return m;
+    }
+}
+
 // The absmax of every block of the requant input and its scale.
 template <int B, bool RQ, bool EF, bool EXACT, typename G = DrGeomOf<B, RQ, EF>>
 __device__ __forceinline__ void rq_scales(const float (&c)[G::U][G::VEC],
                                           BlockScale (&bs)[G::SPB == 1 ? G::U : G::BPT]) {
-    constexpr int V = G::VEC;
     if constexpr (G::SPB == 1) {
 #pragma unroll
-        for (int u = 0; u < G::U; ++u) {
-            uint32_t m = 0;
-#pragma unroll
-            for (int j = 0; j < V; ++j)
-                m = max(m, absbits(c[u][j]));
-            bs[u] = rq_block_scale<7, EXACT>(group_max<G::LPB>(m));
-        }
+        for (int u = 0; u < G::U; ++u)
+            bs[u] = rq_block_scale<7, EXACT>(group_max<G::LPB>(lane_absmax(c[u], 0u)));
     } else {
 #pragma unroll
         for (int b = 0; b < G::BPT; ++b) {
             uint32_t m = 0;
 #pragma unroll
             for (int u = b * G::SPB; u < (b + 1) * G::SPB; ++u)
-#pragma unroll
-                for (int j = 0; j < V; ++j)
-                    m = max(m, absbits(c[u][j]));
+                m = lane_absmax(c[u], m);
             bs[b] = rq_block_scale<7, EXACT>(group_max<kWave>(m));
         }
     }
