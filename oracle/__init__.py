@@ -9,8 +9,8 @@ definitions state).  Each function below names the passage it follows; the C
 source holds the full statement.
 
 Host arrays only: fp32 data as ``np.float32``, bf16 data as ``np.uint16`` bit
-patterns, int4 codes as ``np.uint8`` (two per byte, low nibble first), int8
-codes as ``np.int8``.
+patterns, fp16 data as ``np.float16``, int4 codes as ``np.uint8`` (two per
+byte, low nibble first), int8 codes as ``np.int8``.
 """
 from __future__ import annotations
 
@@ -54,6 +54,10 @@ def lib():
         L.orc_dequant_int8.restype = i32
         L.orc_bf16_rne.argtypes = [f32]
         L.orc_bf16_rne.restype = C.c_uint16
+        L.orc_f16_rne.argtypes = [f32]
+        L.orc_f16_rne.restype = C.c_uint16
+        L.orc_f16_to_f32.argtypes = [C.c_uint16]
+        L.orc_f16_to_f32.restype = f32
         L.orc_philox4x32_10.argtypes = [vp, vp, vp]
         L.orc_philox4x32_10.restype = None
         L.orc_sr_r16.argtypes = [u64, u64]
@@ -86,6 +90,20 @@ def _ptr(a: np.ndarray | None):
         return None
     assert a.flags["C_CONTIGUOUS"], "oracle arrays must be contiguous"
     return a.ctypes.data
+
+
+# Element-type codes of the C oracle's data streams.
+F32, BF16, F16 = 0, 1, 2
+
+
+def _dtype_code(a: np.ndarray, what: str) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.float16:
+        return F16
+    raise TypeError(f"{what} must be float32, uint16 (bf16 bits) or float16")
 
 
 def _check_block(block: int):
@@ -121,23 +139,18 @@ def int4_decode(codes: np.ndarray, n: int) -> np.ndarray:
 def quantize_ef_int4(g: np.ndarray, ef: np.ndarray | None, block: int, beta_e: float,
                      beta_r: float):
     """LoCo error-feedback int4 quantize ("Merge LoCo with Zero++", Overview
-    and review thread).  g: float32 or uint16 (bf16 bits).  ef (float32) is
-    updated in place when given.  Returns (codes uint8[ceil(n/2)],
-    scales float32[ceil(n/block)])."""
+    and review thread).  g: float32, uint16 (bf16 bits) or float16.  ef
+    (float32) is updated in place when given.  Returns (codes
+    uint8[ceil(n/2)], scales float32[ceil(n/block)])."""
     _check_block(block)
     g = np.ascontiguousarray(g)
-    if g.dtype == np.uint16:
-        is_bf16 = 1
-    elif g.dtype == np.float32:
-        is_bf16 = 0
-    else:
-        raise TypeError("g must be float32 or uint16 (bf16 bits)")
+    code = _dtype_code(g, "g")
     n = g.size
     if ef is not None:
         assert ef.dtype == np.float32 and ef.size == n and ef.flags["C_CONTIGUOUS"]
     codes = np.full(int4_code_bytes(n), _POISON_U8, dtype=np.uint8)
     scales = np.full(num_blocks(n, block), np.nan, dtype=np.float32)
-    _ok(lib().orc_quantize_ef_int4(_ptr(g), is_bf16, _ptr(ef), n, block, beta_e, beta_r,
+    _ok(lib().orc_quantize_ef_int4(_ptr(g), code, _ptr(ef), n, block, beta_e, beta_r,
                                    _ptr(codes), _ptr(scales)), "quantize_ef_int4")
     return codes, scales
 
@@ -207,33 +220,46 @@ def dequant_reduce_segments(segments, P: int, block: int, alpha: float, want_out
 
 
 def quant_int8(w: np.ndarray, block: int):
-    """qwZ int8 block quantization ([ZeRO++] notes, section 1.2).  w float32
-    or uint16 (bf16 bits).  Returns (codes int8[n], scales float32[nb])."""
+    """qwZ int8 block quantization ([ZeRO++] notes, section 1.2).  w float32,
+    uint16 (bf16 bits) or float16.  Returns (codes int8[n], scales
+    float32[nb])."""
     _check_block(block)
     w = np.ascontiguousarray(w)
-    is_bf16 = 1 if w.dtype == np.uint16 else 0
-    if not is_bf16 and w.dtype != np.float32:
-        raise TypeError("w must be float32 or uint16 (bf16 bits)")
+    code = _dtype_code(w, "w")
     codes = np.full(w.size, -86, dtype=np.int8)
     scales = np.full(num_blocks(w.size, block), np.nan, dtype=np.float32)
-    _ok(lib().orc_quant_int8(_ptr(w), is_bf16, w.size, block, _ptr(codes), _ptr(scales)),
+    _ok(lib().orc_quant_int8(_ptr(w), code, w.size, block, _ptr(codes), _ptr(scales)),
         "quant_int8")
     return codes, scales
 
 
-def dequant_int8(codes: np.ndarray, scales: np.ndarray, block: int, out_bf16: bool):
-    """qwZ dequantize after the all-gather.  Returns float32[n] or uint16[n]
-    (bf16 bits, round to nearest even)."""
+def dequant_int8(codes: np.ndarray, scales: np.ndarray, block: int, out_bf16: bool = False,
+                 out_f16: bool = False):
+    """qwZ dequantize after the all-gather.  Returns float32[n], uint16[n]
+    (bf16 bits) or float16[n], the 16-bit forms rounded to nearest even."""
+    assert not (out_bf16 and out_f16)
     codes = np.ascontiguousarray(codes, dtype=np.int8)
     scales = np.ascontiguousarray(scales, dtype=np.float32)
-    out = np.zeros(codes.size, dtype=np.uint16 if out_bf16 else np.float32)
-    _ok(lib().orc_dequant_int8(_ptr(codes), _ptr(scales), codes.size, block, _ptr(out),
-                               1 if out_bf16 else 0), "dequant_int8")
+    dt, code = ((np.uint16, BF16) if out_bf16 else (np.float16, F16) if out_f16
+                else (np.float32, F32))
+    out = np.zeros(codes.size, dtype=dt)
+    _ok(lib().orc_dequant_int8(_ptr(codes), _ptr(scales), codes.size, block, _ptr(out), code),
+        "dequant_int8")
     return out
 
 
 def bf16_rne(x: float) -> int:
     return int(lib().orc_bf16_rne(float(x)))
+
+
+def f16_rne(x: float) -> int:
+    """fp32 -> IEEE binary16 bits, round to nearest even."""
+    return int(lib().orc_f16_rne(float(x)))
+
+
+def f16_to_f32(h: int) -> float:
+    """IEEE binary16 bits -> fp32 (exact)."""
+    return float(lib().orc_f16_to_f32(int(h)))
 
 
 def philox4x32_10(ctr, key):
@@ -321,19 +347,14 @@ def quantize_ef_int4_permuted(g, ef, block: int, beta_e: float, beta_r: float, s
     slot_of_part[p] would be.  Partitions are equal and whole blocks long."""
     _check_block(block)
     g = np.ascontiguousarray(g)
-    if g.dtype == np.uint16:
-        is_bf16 = 1
-    elif g.dtype == np.float32:
-        is_bf16 = 0
-    else:
-        raise TypeError("g must be float32 or uint16 (bf16 bits)")
+    code = _dtype_code(g, "g")
     n = g.size
     if ef is not None:
         assert ef.dtype == np.float32 and ef.size == n and ef.flags["C_CONTIGUOUS"]
     slots = np.ascontiguousarray(slot_of_part, dtype=np.uint32)
     codes = np.full(int4_code_bytes(n), _POISON_U8, dtype=np.uint8)
     scales = np.full(num_blocks(n, block), np.nan, dtype=np.float32)
-    _ok(lib().orc_quantize_ef_int4_permuted(_ptr(g), is_bf16, _ptr(ef), n, block, beta_e, beta_r,
+    _ok(lib().orc_quantize_ef_int4_permuted(_ptr(g), code, _ptr(ef), n, block, beta_e, beta_r,
                                             slots.size, _ptr(slots), _ptr(codes), _ptr(scales)),
         "quantize_ef_int4_permuted")
     return codes, scales

@@ -29,7 +29,8 @@
  *   orc_quant_block, orc_quantize_ef_int4, orc_quantize_ef_int4_permuted,
  *   orc_zeropp_slots, orc_dequant_reduce, orc_dequant_reduce_segments,
  *   orc_quant_int8, orc_dequant_int8,
- *   orc_bf16_rne, orc_sr_round, orc_philox4x32_10, orc_sr_accumulate,
+ *   orc_bf16_rne, orc_f16_rne, orc_f16_to_f32, orc_sr_round,
+ *   orc_philox4x32_10, orc_sr_accumulate,
  *   orc_sr_accumulate_segments, orc_volume_bytes: pinned.
  *
  * Every entry point that takes buffers checks its arguments first and
@@ -47,6 +48,15 @@
 #define ORC_EINVAL (-1)
 
 static int bad_block(uint32_t block) { return block < 2 || block > 4096 || (block & 1u); }
+
+/* Element types of the 16- and 32-bit data streams (the int4 path's g, the
+ * int8 path's w and its dequantized output): IEEE binary32, bf16 (the top
+ * half of a binary32 pattern) and IEEE binary16. */
+#define ORC_F32 0
+#define ORC_BF16 1
+#define ORC_F16 2
+
+static int bad_dtype(int dtype) { return dtype != ORC_F32 && dtype != ORC_BF16 && dtype != ORC_F16; }
 
 /* ---------------------------------------------------------------- bf16 -- */
 
@@ -80,6 +90,67 @@ uint16_t orc_bf16_rne(float f)
     u += 0x7FFFu + keep_lsb;
     return (uint16_t)(u >> 16);
 }
+
+/* ---------------------------------------------------------------- fp16 -- */
+
+/* IEEE 754 binary16: sign bit, 5 exponent bits with bias 15, 10 fraction
+ * bits.  Exponent field 0 holds zero and the subnormals f * 2^-24, field 31
+ * infinity (f = 0) and NaN.  Widening to binary32 is exact: a normal value is
+ * (1024 + f) * 2^(e - 25), which binary32 holds; a NaN keeps its sign and
+ * payload (shifted into the top of the binary32 fraction) and is quiet. */
+static float f16_to_f32(uint16_t h)
+{
+    uint32_t sign = (uint32_t)(h >> 15) & 1u, e = (uint32_t)(h >> 10) & 0x1Fu, f = h & 0x3FFu;
+    float v;
+    if (e == 31) {
+        uint32_t u = (sign << 31) | 0x7F800000u | (f << 13) | (f ? 0x00400000u : 0u);
+        memcpy(&v, &u, sizeof v);
+        return v;
+    }
+    if (e == 0)
+        v = ldexpf((float)f, -24);
+    else
+        v = ldexpf((float)(f | 0x400u), (int)e - 25);
+    return sign ? -v : v;
+}
+
+/* fp32 -> fp16, round to nearest, ties to even, from the definition: count
+ * the value in units of the result's last place (2^-24 below 2^-14, the
+ * subnormal range; 2^(E-10) for 2^E <= |x| < 2^(E+1)), which is an exact
+ * power-of-two scaling, round that count to an integer (rintf, ties to even),
+ * and assemble the pattern; a count that rounds up to the next power of two
+ * carries into the exponent field by plain addition.  |x| >= 65520 (half an
+ * ulp above the largest finite 65504) rounds to infinity; NaN becomes the
+ * quiet NaN 0x7E00 with x's sign. */
+uint16_t orc_f16_rne(float x)
+{
+    uint16_t sign = (uint16_t)((f32_bits(x) >> 16) & 0x8000u);
+    if (isnan(x))
+        return (uint16_t)(sign | 0x7E00u);
+    float a = fabsf(x);
+    if (a >= 65520.0f)
+        return (uint16_t)(sign | 0x7C00u);
+    if (a < 0x1p-14f)
+        return (uint16_t)(sign | (uint16_t)rintf(a * 0x1p24f));
+    int E;
+    frexpf(a, &E); /* a = m 2^E, m in [0.5, 1): 2^(E-1) <= a < 2^E */
+    E -= 1;
+    uint32_t q = (uint32_t)rintf(ldexpf(a, 10 - E)); /* in [1024, 2048] */
+    return (uint16_t)(sign | ((((uint32_t)(E + 15)) << 10) + (q - 1024u)));
+}
+
+/* One element of a data stream of the given type, widened to fp32. */
+static float load_elem(const void *p, int dtype, size_t i)
+{
+    if (dtype == ORC_BF16)
+        return bf16_to_f32(((const uint16_t *)p)[i]);
+    if (dtype == ORC_F16)
+        return f16_to_f32(((const uint16_t *)p)[i]);
+    return ((const float *)p)[i];
+}
+
+/* fp16 exports for the pins: widening and rounding of one value. */
+float orc_f16_to_f32(uint16_t h) { return f16_to_f32(h); }
 
 /* ---------------------------------------------------- block quantizer -- */
 
@@ -145,14 +216,15 @@ int32_t orc_int4_decode(const uint8_t *codes, size_t i) { return get_nibble(code
  *   d  = fl(k * s)
  *   r  = fl(c - d)
  *   e' = fl(fl(beta_e * e) + fl(beta_r * r))     (only with an EF buffer)
- * g is fp32 (g_is_bf16 == 0) or bf16 bit patterns (g_is_bf16 != 0).
+ * g holds fp32, bf16 or fp16 values (g_dtype ORC_F32, ORC_BF16, ORC_F16);
+ * 16-bit values are widened to fp32 exactly before anything else.
  * codes: ceil(n/2) bytes, scales: ceil(n/block) floats, ef: n floats or NULL.
  * block must be even and at most 4096.  The last block may be partial; its
  * scale uses only its own elements. */
-int orc_quantize_ef_int4(const void *g, int g_is_bf16, float *ef, size_t n, uint32_t block,
+int orc_quantize_ef_int4(const void *g, int g_dtype, float *ef, size_t n, uint32_t block,
                          float beta_e, float beta_r, uint8_t *codes, float *scales)
 {
-    if (bad_block(block) || (n > 0 && (!g || !codes || !scales)))
+    if (bad_block(block) || bad_dtype(g_dtype) || (n > 0 && (!g || !codes || !scales)))
         return ORC_EINVAL;
     float c[4096];
     int32_t k[4096];
@@ -162,7 +234,7 @@ int orc_quantize_ef_int4(const void *g, int g_is_bf16, float *ef, size_t n, uint
         size_t m = n - lo < block ? n - lo : block;
         for (size_t j = 0; j < m; j++) {
             size_t i = lo + j;
-            float gi = g_is_bf16 ? bf16_to_f32(((const uint16_t *)g)[i]) : ((const float *)g)[i];
+            float gi = load_elem(g, g_dtype, i);
             c[j] = ef ? gi + ef[i] : gi;
         }
         float s;
@@ -212,11 +284,12 @@ int orc_zeropp_slots(uint32_t intra, uint32_t inter, uint32_t *slot_of_part)
  * elements within the whole buffer (its blocks are the same blocks), and
  * its codes and scales are stored where partition slot_of_part[p] lies in
  * that function's layout.  g and ef keep their natural order. */
-int orc_quantize_ef_int4_permuted(const void *g, int g_is_bf16, float *ef, size_t n,
+int orc_quantize_ef_int4_permuted(const void *g, int g_dtype, float *ef, size_t n,
                                   uint32_t block, float beta_e, float beta_r, uint32_t n_part,
                                   const uint32_t *slot_of_part, uint8_t *codes, float *scales)
 {
-    if (bad_block(block) || n_part < 1 || !slot_of_part || !g || !codes || !scales)
+    if (bad_block(block) || bad_dtype(g_dtype) || n_part < 1 || !slot_of_part || !g || !codes ||
+        !scales)
         return ORC_EINVAL;
     size_t part = n / n_part;
     if (part * n_part != n || part % block != 0)
@@ -231,9 +304,9 @@ int orc_quantize_ef_int4_permuted(const void *g, int g_is_bf16, float *ef, size_
     for (uint32_t p = 0; p < n_part; p++) {
         size_t from = p * part;
         size_t to = slot_of_part[p] * part;
-        const void *gp = g_is_bf16 ? (const void *)((const uint16_t *)g + from)
-                                   : (const void *)((const float *)g + from);
-        int rc = orc_quantize_ef_int4(gp, g_is_bf16, ef ? ef + from : NULL, part, block, beta_e,
+        const void *gp = g_dtype == ORC_F32 ? (const void *)((const float *)g + from)
+                                            : (const void *)((const uint16_t *)g + from);
+        int rc = orc_quantize_ef_int4(gp, g_dtype, ef ? ef + from : NULL, part, block, beta_e,
                                       beta_r, codes + to / 2, scales + to / block);
         if (rc)
             return rc;
@@ -320,12 +393,13 @@ int orc_dequant_reduce_segments(uint32_t n_seg, const uint8_t *const *codes,
 /* ------------------------------------------------ qwZ int8 weights -- */
 
 /* Block int8 weight quantization before the forward all-gather ([ZeRO++]
- * section 1.2, qwZ): the block quantizer with qmax = 127, one fp32 scale per
- * block, codes stored as int8. */
-int orc_quant_int8(const void *w, int w_is_bf16, size_t n, uint32_t block, int8_t *codes,
+ * section 1.2, qwZ, whose weights are fp16): the block quantizer with
+ * qmax = 127, one fp32 scale per block, codes stored as int8.  w holds fp32,
+ * bf16 or fp16 values (w_dtype), widened to fp32 exactly. */
+int orc_quant_int8(const void *w, int w_dtype, size_t n, uint32_t block, int8_t *codes,
                    float *scales)
 {
-    if (bad_block(block) || (n > 0 && (!w || !codes || !scales)))
+    if (bad_block(block) || bad_dtype(w_dtype) || (n > 0 && (!w || !codes || !scales)))
         return ORC_EINVAL;
     float x[4096];
     int32_t k[4096];
@@ -334,7 +408,7 @@ int orc_quant_int8(const void *w, int w_is_bf16, size_t n, uint32_t block, int8_
         size_t lo = b * (size_t)block;
         size_t m = n - lo < block ? n - lo : block;
         for (size_t j = 0; j < m; j++)
-            x[j] = w_is_bf16 ? bf16_to_f32(((const uint16_t *)w)[lo + j]) : ((const float *)w)[lo + j];
+            x[j] = load_elem(w, w_dtype, lo + j);
         orc_quant_block(x, m, 127, k, &scales[b]);
         for (size_t j = 0; j < m; j++)
             codes[lo + j] = (int8_t)k[j];
@@ -342,17 +416,19 @@ int orc_quant_int8(const void *w, int w_is_bf16, size_t n, uint32_t block, int8_
     return 0;
 }
 
-/* Dequantize after the all-gather: w' = fl(k * s), stored as fp32 or as
- * bf16 rounded to nearest even from that fp32 value. */
+/* Dequantize after the all-gather: w' = fl(k * s), stored as fp32, or as
+ * bf16 or fp16 rounded to nearest even from that fp32 value (out_dtype). */
 int orc_dequant_int8(const int8_t *codes, const float *scales, size_t n, uint32_t block,
-                     void *out, int out_is_bf16)
+                     void *out, int out_dtype)
 {
-    if (block < 1 || (n > 0 && (!codes || !scales || !out)))
+    if (block < 1 || bad_dtype(out_dtype) || (n > 0 && (!codes || !scales || !out)))
         return ORC_EINVAL;
     for (size_t i = 0; i < n; i++) {
         float v = (float)codes[i] * scales[i / block];
-        if (out_is_bf16)
+        if (out_dtype == ORC_BF16)
             ((uint16_t *)out)[i] = orc_bf16_rne(v);
+        else if (out_dtype == ORC_F16)
+            ((uint16_t *)out)[i] = orc_f16_rne(v);
         else
             ((float *)out)[i] = v;
     }

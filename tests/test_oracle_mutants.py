@@ -46,6 +46,23 @@ MUTANTS = [
     ("bf16 rounding ties away", "u += 0x7FFFu + keep_lsb;", "u += 0x8000u;"),
     ("int8 dequant truncates to bf16", "((uint16_t *)out)[i] = orc_bf16_rne(v);",
      "((uint16_t *)out)[i] = (uint16_t)(f32_bits(v) >> 16);"),
+    ("fp16 widening exponent bias", "ldexpf((float)(f | 0x400u), (int)e - 25)",
+     "ldexpf((float)(f | 0x400u), (int)e - 24)"),
+    ("fp16 subnormals widened with the implicit bit", "v = ldexpf((float)f, -24);",
+     "v = ldexpf((float)(f | 0x400u), -24);"),
+    ("fp16 rounding truncates", "uint32_t q = (uint32_t)rintf(ldexpf(a, 10 - E));",
+     "uint32_t q = (uint32_t)truncf(ldexpf(a, 10 - E));"),
+    ("fp16 rounding ties away", "uint32_t q = (uint32_t)rintf(ldexpf(a, 10 - E));",
+     "uint32_t q = (uint32_t)roundf(ldexpf(a, 10 - E));"),
+    ("fp16 overflow at the largest finite", "if (a >= 65520.0f)", "if (a > 65504.0f)"),
+    ("fp16 subnormal range one binade short", "if (a < 0x1p-14f)", "if (a < 0x1p-15f)"),
+    ("fp16 normal results lose the sign",
+     "return (uint16_t)(sign | ((((uint32_t)(E + 15)) << 10) + (q - 1024u)));",
+     "return (uint16_t)((((uint32_t)(E + 15)) << 10) + (q - 1024u));"),
+    ("int8 dequant fp16 output rounded as bf16", "((uint16_t *)out)[i] = orc_f16_rne(v);",
+     "((uint16_t *)out)[i] = orc_bf16_rne(v);"),
+    ("fp16 input read as bf16", "return f16_to_f32(((const uint16_t *)p)[i]);",
+     "return bf16_to_f32(((const uint16_t *)p)[i]);"),
     ("Philox key schedule", "k1 += PHILOX_W1;", "k1 += PHILOX_W0;"),
     ("Philox multipliers swapped", "uint64_t p0 = (uint64_t)PHILOX_M0 * (uint64_t)x0;",
      "uint64_t p0 = (uint64_t)PHILOX_M1 * (uint64_t)x0;"),

@@ -249,6 +249,27 @@ def test_bf16_input_is_widened_exactly():
     assert (c1 == c2).all() and (s1 == s2).all() and (e1.view(np.uint32) == e2.view(np.uint32)).all()
 
 
+def test_f16_input_is_widened_exactly():
+    """fp16 gradients and weights are widened to fp32 exactly before the
+    quantizers see them: the same outputs as from the widened fp32 array."""
+    n, B = 1000, 64
+    g16 = (RNG.standard_normal(n) * 1e-3).astype(np.float16)  # includes fp16 subnormals
+    g16[:4] = [np.float16(6e-8), np.float16(-6e-8), np.float16(65504.0), np.float16(-0.0)]
+    e1 = (RNG.standard_normal(n) * 1e-4).astype(np.float32)
+    e2 = e1.copy()
+    c1, s1 = O.quantize_ef_int4(g16, e1, B, 0.9, 1.0)
+    c2, s2 = O.quantize_ef_int4(g16.astype(np.float32), e2, B, 0.9, 1.0)
+    assert (c1 == c2).all() and (s1.view(np.uint32) == s2.view(np.uint32)).all()
+    assert (e1.view(np.uint32) == e2.view(np.uint32)).all()
+    k1, t1 = O.quant_int8(g16, 128)
+    k2, t2 = O.quant_int8(g16.astype(np.float32), 128)
+    assert (k1 == k2).all() and (t1.view(np.uint32) == t2.view(np.uint32)).all()
+    slots = [2, 0, 3, 1]
+    p1 = O.quantize_ef_int4_permuted(g16[:512], None, 32, 0.9, 1.0, slots)
+    p2 = O.quantize_ef_int4_permuted(g16[:512].astype(np.float32), None, 32, 0.9, 1.0, slots)
+    assert (p1[0] == p2[0]).all() and (p1[1].view(np.uint32) == p2[1].view(np.uint32)).all()
+
+
 # ---------------------------------------------------- error feedback (LoCo) --
 
 @pytest.mark.parametrize("gdtype", ["fp32", "bf16"])
@@ -468,6 +489,61 @@ def test_bf16_rne_matches_torch_and_worked_examples(golden_dir):
 
 
 # ------------------------------------------------------ stochastic rounding --
+
+def test_f16_worked_examples(golden_dir):
+    G = load(golden_dir, "f16_worked_examples.json")
+    for c in G["rne"]:
+        assert O.f16_rne(bits_f32(int(c["x"], 16))) == int(c["out"], 16), c
+    for c in G["widen"]:
+        assert f32_bits(O.f16_to_f32(int(c["h"], 16))) == int(c["out"], 16), c
+
+
+def test_f16_widening_exhaustive_matches_numpy():
+    """All 65,536 fp16 patterns against numpy's float16 -> float32."""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = h.view(np.float16).astype(np.float32)
+    got = np.array([O.f16_to_f32(int(v)) for v in h], dtype=np.float32)
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all()
+    assert (got[~nan].view(np.uint32) == ref[~nan].view(np.uint32)).all()
+    assert (np.signbit(got[nan]) == np.signbit(ref[nan])).all()
+
+
+def test_f16_rne_matches_numpy_at_every_boundary():
+    """fp32 -> fp16 against numpy's float32 -> float16 (round to nearest even)
+    at every finite fp16 value, every midpoint between neighbours (exact in
+    fp32, so each is a true tie), one fp32 ulp either side of each midpoint,
+    both signs, the specials and 100,000 random fp32 patterns."""
+    h = np.arange(0, 0x7C00, dtype=np.uint32).astype(np.uint16)
+    v = h.view(np.float16).astype(np.float32)
+    nxt = np.append(v[1:], np.float32(65536.0))
+    mid64 = (v.astype(np.float64) + nxt.astype(np.float64)) / 2
+    mid = mid64.astype(np.float32)
+    assert (mid.astype(np.float64) == mid64).all()  # the midpoints are exact
+    x = np.concatenate([v, mid, np.nextafter(mid, np.float32(0)), np.nextafter(mid, np.float32(np.inf))])
+    rnd = RNG.integers(0, 2 ** 32, size=100000, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    x = np.concatenate([x, -x, rnd, np.array([np.inf, -np.inf, np.nan, 1e30, -1e30], np.float32)])
+    with np.errstate(over="ignore", invalid="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    got = np.array([O.f16_rne(t) for t in x], dtype=np.uint16)
+    nan = np.isnan(x)
+    assert (got[~nan] == ref[~nan]).all()
+    assert ((got[nan] & 0x7C00) == 0x7C00).all() and ((got[nan] & 0x3FF) != 0).all()
+
+
+def test_int8_dequant_f16_is_rne_of_the_fp32_product():
+    n, B = 4096 + 77, 256
+    w = (RNG.standard_normal(n) * 3.0).astype(np.float32)
+    w[:3] = [70000.0, -70000.0, 1e-9]
+    codes, scales = O.quant_int8(w, B)
+    out = O.dequant_int8(codes, scales, B, out_f16=True)
+    prod = codes.astype(np.float32) * np.repeat(scales, B)[:n]
+    with np.errstate(over="ignore"):
+        ref = prod.astype(np.float16)
+    assert out.dtype == np.float16
+    assert (out.view(np.uint16) == ref.view(np.uint16)).all()
+    assert np.isinf(out[:2]).all()  # 70000 is past the fp16 range
+
 
 def test_philox_known_answers(golden_dir):
     G = load(golden_dir, "philox4x32_10_kat.json")
