@@ -690,6 +690,14 @@ def extra_rows(torch, zq, synth, dev, log, cpu=True):
     ms = timed_burst(torch, lambda: zq.zq_dequant_int8(c8, s8, 2048, wd), 20)
     rows["dequant_int8_bf16_b2048_0.85B"] = row(n * 3 + 4 * s8.numel(), ms, n)
     log("int8 rows", rows["quant_int8_bf16_b2048_0.85B"], rows["dequant_int8_bf16_b2048_0.85B"])
+    # the same with the pages' fp16 weights (qwZ: fp16 -> int8 -> fp16)
+    wh = torch.empty(n, dtype=torch.float16, device=dev)
+    wh.copy_(w)
+    ms = timed_burst(torch, lambda: zq.zq_quant_int8(wh, 2048, c8, s8), 20)
+    rows["quant_int8_fp16_b2048_0.85B"] = row(n * 3 + 4 * s8.numel(), ms, n)
+    ms = timed_burst(torch, lambda: zq.zq_dequant_int8(c8, s8, 2048, wh), 20)
+    rows["dequant_int8_fp16_b2048_0.85B"] = row(n * 3 + 4 * s8.numel(), ms, n)
+    del wh
     if cpu:
         S = 1 << 27
         wh = to_host_np(w[:S])

@@ -37,7 +37,8 @@
  *     arithmetic but are outside the supported contract.
  *   - Arithmetic is IEEE binary32, round to nearest even, no fused
  *     multiply-add, denormals kept; integer codes, scales (as bits), error-
- *     feedback buffers and bf16 outputs are bit-exact functions of the inputs.
+ *     feedback buffers and bf16 / fp16 outputs are bit-exact functions of the
+ *     inputs.
  *
  * Layouts
  *   int4 codes: two's-complement nibbles, element 2j in the low nibble of
@@ -46,7 +47,7 @@
  *   scales: one fp32 per block of `block` consecutive elements,
  *     ceil(n/block) of them; a partial last block's scale covers only its
  *     own elements.
- *   bf16: uint16 bit patterns.
+ *   bf16, fp16: uint16 bit patterns.
  */
 #ifndef ZQ_H
 #define ZQ_H
@@ -72,7 +73,10 @@ typedef enum {
     ZQ_ERR_LAUNCH = 8  /* the HIP kernel launch itself failed             */
 } zq_status;
 
-typedef enum { ZQ_FP32 = 0, ZQ_BF16 = 1 } zq_dtype;
+/* Element type of a data stream: IEEE binary32, bf16 (the top half of a
+ * binary32 pattern) or IEEE binary16.  16-bit inputs are widened to fp32
+ * exactly; 16-bit outputs are rounded to nearest even from fp32. */
+typedef enum { ZQ_FP32 = 0, ZQ_BF16 = 1, ZQ_FP16 = 2 } zq_dtype;
 
 /*
  * zq_quantize_ef_int4 -- block int4 gradient quantization with LoCo error
@@ -89,7 +93,8 @@ typedef enum { ZQ_FP32 = 0, ZQ_BF16 = 1 } zq_dtype;
  * LoCo's literal update is beta_e = beta, beta_r = 1; plain error feedback is
  * (0, 1); a moving-average reading is (beta, 1 - beta).
  *
- *   g       [n] fp32 or bf16 (g_dtype), read only.
+ *   g       [n] fp32, bf16 or fp16 (g_dtype; the LoCo kernel's gradients are
+ *           half precision, [LoCo] review thread), read only.
  *   ef      [n] fp32, read-modify-write in place; NULL for no error feedback.
  *   codes   [ceil(n/2)] bytes, written.     scales [ceil(n/block)] fp32, written.
  * Errors: NULL g/codes/scales; bad dtype or block; misalignment; codes or
@@ -231,7 +236,8 @@ zq_status zq_dequant_reduce_batched(const zq_dr_segment *segs, uint32_t n_seg, u
  * forward all-gather ([ZeRO++] section 1.2: fp16 to int8, an independent
  * quantization per block of parameters for accuracy).
  *   s = fl(max|w| / 127);  k_i = 0 if s == 0 else clamp(rne(fl(w_i / s)), -127, 127)
- *   w      [n] fp32 or bf16 (w_dtype), read only.
+ *   w      [n] fp32, bf16 or fp16 (w_dtype; the pages' qwZ weights are fp16),
+ *          read only.
  *   codes  [n] int8 written.   scales [ceil(n/block)] fp32 written.
  */
 zq_status zq_quant_int8(const void *w, zq_dtype w_dtype, size_t n, uint32_t block, int8_t *codes,
@@ -239,9 +245,12 @@ zq_status zq_quant_int8(const void *w, zq_dtype w_dtype, size_t n, uint32_t bloc
 
 /*
  * zq_dequant_int8 -- qwZ receive side: w'_i = fl(k_i * s_b), stored as fp32
- * or rounded to nearest even bf16 ([ZeRO++] section 1.2).
+ * or rounded to nearest even bf16 or fp16 ([ZeRO++] section 1.2: the weights
+ * return to fp16 for the layer's compute); fp16 results from 65520 in
+ * magnitude up are infinite.
  *   codes [n] int8, scales [ceil(n/block)] fp32, read only.
- *   out   [n] fp32 or bf16 (out_dtype), written; must not overlap the inputs.
+ *   out   [n] fp32, bf16 or fp16 (out_dtype), written; must not overlap the
+ *         inputs.
  */
 zq_status zq_dequant_int8(const int8_t *codes, const float *scales, size_t n, uint32_t block,
                           void *out, zq_dtype out_dtype, void *stream);

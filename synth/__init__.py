@@ -118,7 +118,7 @@ def _fill_normal(out: torch.Tensor, std: float, gen: torch.Generator, heavy: boo
 
 def fill_model(out: torch.Tensor, tensors: list[Tensor] | None, std: float, seed: int,
                heavy_tails: bool = False, slab: int = 1 << 27) -> None:
-    """Fill a flat buffer (fp32 or bf16) in place with a gradient/weight of
+    """Fill a flat buffer (fp32, bf16 or fp16) in place with a gradient/weight of
     the given tensor table.  Values are drawn in fp32 slab by slab and cast to
     the buffer's dtype with torch's round-to-nearest-even conversion."""
     n = out.numel()

@@ -57,6 +57,8 @@ def bits(a: np.ndarray) -> np.ndarray:
     a = np.ascontiguousarray(a)
     if a.dtype == np.float32:
         return a.view(np.uint32)
+    if a.dtype == np.float16:
+        return a.view(np.uint16)
     return a
 
 
@@ -110,6 +112,28 @@ def grad_values(n: int, seed: int, std: float = 1e-3, outlier_p: float = 0.01,
 
 def as_bf16_bits(x: np.ndarray) -> np.ndarray:
     return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def as_f16(x: np.ndarray, seed: int = 0) -> np.ndarray:
+    """fp16 inputs from fp32 values: clipped to the finite fp16 range (inputs
+    are expected finite), rounded to nearest even, with a few fp16-specific
+    values planted: subnormals, the largest finite value and signed zeros."""
+    h = np.clip(x, -60000.0, 60000.0).astype(np.float16)
+    if h.size >= 8:
+        rng = np.random.default_rng(seed)
+        idx = rng.choice(h.size, size=min(h.size, 16), replace=False)
+        sub = np.array([6e-8, -6e-8, 3e-5, -1.2e-7, 65504.0, -0.0, 0.0, 6.1e-5], np.float16)
+        h[idx] = sub[np.arange(idx.size) % sub.size]
+    return h
+
+
+def as_dtype(x: np.ndarray, dt: str, seed: int = 0) -> np.ndarray:
+    """fp32 values as the host form of dtype dt: float32, bf16 bits or fp16."""
+    if dt == "bf16":
+        return as_bf16_bits(x)
+    if dt == "fp16":
+        return as_f16(x, seed)
+    return x
 
 
 def bf16_to_f32(h: np.ndarray) -> np.ndarray:

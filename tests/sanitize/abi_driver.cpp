@@ -24,13 +24,13 @@ static int launches = 0;
     } while (0)
 
 namespace zq {
-hipError_t launch_quantize_ef_int4(const void* g, bool, float*, size_t n, uint32_t, float, float,
+hipError_t launch_quantize_ef_int4(const void* g, int, float*, size_t n, uint32_t, float, float,
                                    uint8_t* codes, float* scales, hipStream_t) {
     CHECK(g && codes && scales && n > 0);
     launches++;
     return hipSuccess;
 }
-hipError_t launch_quantize_ef_int4_permuted(const void* g, bool, float*, size_t n, uint32_t block,
+hipError_t launch_quantize_ef_int4_permuted(const void* g, int, float*, size_t n, uint32_t block,
                                             float, float, uint8_t*, float*, const PartPerm& perm,
                                             hipStream_t) {
     CHECK(g && perm.n_part >= 1 && perm.n_part <= kMaxParts);
@@ -38,7 +38,7 @@ hipError_t launch_quantize_ef_int4_permuted(const void* g, bool, float*, size_t 
     launches++;
     return hipSuccess;
 }
-hipError_t launch_quantize_ef_int4_batched(const EfqSegment* segs, uint32_t n_seg, bool, bool,
+hipError_t launch_quantize_ef_int4_batched(const EfqSegment* segs, uint32_t n_seg, int, bool,
                                            uint32_t, float, float, hipStream_t) {
     uint64_t sum = 0;
     for (uint32_t i = 0; i < n_seg; ++i)
@@ -62,11 +62,11 @@ hipError_t launch_dequant_reduce_batched(const DrSegment* segs, uint32_t n_seg,
     launches++;
     return hipSuccess;
 }
-hipError_t launch_quant_int8(const void*, bool, size_t, uint32_t, int8_t*, float*, hipStream_t) {
+hipError_t launch_quant_int8(const void*, int, size_t, uint32_t, int8_t*, float*, hipStream_t) {
     launches++;
     return hipSuccess;
 }
-hipError_t launch_dequant_int8(const int8_t*, const float*, size_t, uint32_t, void*, bool,
+hipError_t launch_dequant_int8(const int8_t*, const float*, size_t, uint32_t, void*, int,
                                hipStream_t) {
     launches++;
     return hipSuccess;

@@ -54,7 +54,11 @@ def efq(g=FAKE, dt=0, ef=None, n=1024, block=128, codes=FAKE + 0x100000, scales=
 
 
 def test_quantize_validation():
-    assert efq(dt=2) == zq.ZQ_ERR_DTYPE
+    assert efq(dt=3) == zq.ZQ_ERR_DTYPE
+    # fp16 (2) is a known dtype: validation goes on, with 2-byte elements
+    assert efq(dt=zq.ZQ_FP16, g=FAKE + 4) == zq.ZQ_ERR_ALIGN
+    assert efq(dt=zq.ZQ_FP16, codes=FAKE + 0x7F0) == zq.ZQ_ERR_ALIAS  # inside g's 2048 bytes
+    assert efq(dt=zq.ZQ_FP32, codes=FAKE + 0xFF0) == zq.ZQ_ERR_ALIAS  # inside g's 4096 bytes
     for b in [0, 16, 100, 8192, 129]:
         assert efq(block=b) == zq.ZQ_ERR_BLOCK
     assert efq(n=(1 << 60) + 1) == zq.ZQ_ERR_SIZE
@@ -107,6 +111,7 @@ def test_int8_and_sr_validation():
     assert q8(w=None) == zq.ZQ_ERR_NULL
     assert q8(codes=FAKE + 0x100008) == zq.ZQ_ERR_ALIGN
     assert q8(codes=FAKE + 0x1000) == zq.ZQ_ERR_ALIAS
+    assert q8(dt=zq.ZQ_FP16, codes=FAKE + 0x1000) == zq.ZQ_ERR_ALIAS  # w is 8 KB of fp16
     dq = lambda **k: L.zq_dequant_int8(k.get("codes", FAKE), k.get("scales", FAKE + 0x100000),
                                        k.get("n", 4096), 2048, k.get("out", FAKE + 0x200000),
                                        k.get("dt", 1), None)
@@ -114,6 +119,7 @@ def test_int8_and_sr_validation():
     assert dq(out=None) == zq.ZQ_ERR_NULL
     assert dq(out=FAKE + 0x200002) == zq.ZQ_ERR_ALIGN
     assert dq(out=FAKE + 0x800) == zq.ZQ_ERR_ALIAS
+    assert dq(dt=zq.ZQ_FP16, out=FAKE + 0x200002) == zq.ZQ_ERR_ALIGN
     sr = lambda **k: L.zq_sr_accumulate(k.get("dst", FAKE), k.get("src", FAKE + 0x100000),
                                         k.get("n", 4096), 1, k.get("cb", 0), 0, None)
     assert sr(n=0, dst=None) == zq.ZQ_OK

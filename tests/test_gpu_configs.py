@@ -194,15 +194,19 @@ def test_sr_past_the_xcd_ordered_map_single_and_batched():
 
 # ------------------------------------------------------------ qwZ 0.85B --
 
-def test_int8_weights_0p85b_sampled_blocks():
+@pytest.mark.parametrize("wdt", [torch.bfloat16, torch.float16])
+def test_int8_weights_0p85b_sampled_blocks(wdt):
+    """qwZ on the 0.85B model's weights, bf16 and the pages' fp16: every
+    output written, sampled blocks (first, last, 254 random) against the
+    oracle, the dequantized weights in the input's dtype."""
     tensors = synth.llama_0p85b()
     n = synth.total(tensors)
     B = 2048
-    w = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    w = torch.empty(n, dtype=wdt, device="cuda")
     synth.fill_model(w, tensors, std=0.02, seed=synth.seed_for("llama0p85b", "weights"))
     codes = torch.empty(n, dtype=torch.int8, device="cuda")
     scales = torch.empty(n // B, dtype=torch.float32, device="cuda")
-    wd = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    wd = torch.empty(n, dtype=wdt, device="cuda")
     # poison: -128 is never a code (clamp to +-127), NaN never a finite block's scale
     codes.fill_(-128)
     scales.fill_(float("nan"))
@@ -220,8 +224,10 @@ def test_int8_weights_0p85b_sampled_blocks():
     c_o, s_o = O.quant_int8(w_h, B)
     assert_bits_equal(gather_blocks(codes, blocks, B).view(np.uint8), c_o.view(np.uint8), "codes")
     assert_bits_equal(to_host(scales)[blocks], s_o, "scales")
-    assert_bits_equal(gather_blocks(wd, blocks, B), O.dequant_int8(c_o, s_o, B, out_bf16=True),
-                      "dequantized bf16")
+    f16 = wdt == torch.float16
+    assert_bits_equal(gather_blocks(wd, blocks, B),
+                      O.dequant_int8(c_o, s_o, B, out_bf16=not f16, out_f16=f16),
+                      f"dequantized {wdt}")
 
 
 # ------------------------------------------- qgZ + LoCo: 0.85B and 7.5B --

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle as O
-from tests.gpu_helpers import (Guarded, as_bf16_bits, assert_bits_equal, bf16_to_f32,
+from tests.gpu_helpers import (Guarded, as_bf16_bits, as_dtype, assert_bits_equal, bf16_to_f32,
                                grad_values, to_gpu, to_host)
 
 pytestmark = pytest.mark.gpu
@@ -66,12 +66,12 @@ def check_efq(g_host, ef_host, block, be, br, what):
 
 
 @pytest.mark.parametrize("block", BLOCKS)
-@pytest.mark.parametrize("gdt", ["fp32", "bf16"])
+@pytest.mark.parametrize("gdt", ["fp32", "bf16", "fp16"])
 @pytest.mark.parametrize("with_ef", [False, True])
 def test_efq_matches_oracle(block, gdt, with_ef):
     for i, n in enumerate(sizes_for(block, 1024)):
         x = grad_values(n, seed=1000 * block + i, special=True, block=block)
-        g = as_bf16_bits(x) if gdt == "bf16" else x
+        g = as_dtype(x, gdt, seed=i)
         ef = (grad_values(n, seed=7 + i, std=1e-5) if with_ef else None)
         check_efq(g, ef, block, 0.9, 1.0, f"efq n={n} B={block} {gdt} ef={with_ef}")
 
@@ -298,11 +298,11 @@ def test_requant_scales_at_the_decode_boundary(with_rq_ef):
 # ---------------------------------------------------------------- qwZ int8 --
 
 @pytest.mark.parametrize("block", BLOCKS)
-@pytest.mark.parametrize("wdt", ["fp32", "bf16"])
+@pytest.mark.parametrize("wdt", ["fp32", "bf16", "fp16"])
 def test_quant_dequant_int8(block, wdt):
     for i, n in enumerate(sizes_for(block, 1024)):
         x = grad_values(n, seed=300 * block + i, std=0.02, special=True, block=block)
-        w = as_bf16_bits(x) if wdt == "bf16" else x
+        w = as_dtype(x, wdt, seed=i)
         c_o, s_o = O.quant_int8(w, block)
         codes = Guarded(n, torch.int8)
         scales = Guarded(-(-n // block), torch.float32)
@@ -312,12 +312,13 @@ def test_quant_dequant_int8(block, wdt):
         c_g, s_g = codes.host(), scales.host()
         assert_bits_equal(c_g.view(np.uint8), c_o.view(np.uint8), what + " codes")
         assert_bits_equal(s_g, s_o, what + " scales")
-        for out_bf16 in (True, False):
-            o_o = O.dequant_int8(c_o, s_o, block, out_bf16=out_bf16)
-            out = Guarded(n, torch.bfloat16 if out_bf16 else torch.float32)
+        for odt, tdt in (("bf16", torch.bfloat16), ("fp16", torch.float16),
+                         ("fp32", torch.float32)):
+            o_o = O.dequant_int8(c_o, s_o, block, out_bf16=odt == "bf16", out_f16=odt == "fp16")
+            out = Guarded(n, tdt)
             Z().zq_dequant_int8(to_gpu(c_o), to_gpu(s_o), block, out.t)
             torch.cuda.synchronize()
-            assert_bits_equal(out.host(), o_o, what + f" dequant bf16={out_bf16}")
+            assert_bits_equal(out.host(), o_o, what + f" dequant to {odt}")
 
 
 # ------------------------------------------------------ stochastic rounding --
@@ -443,16 +444,16 @@ def test_sr_batched_equals_per_tensor_calls():
 # -------------------------------------- permuted (ZeRO++ hierarchical) order --
 
 @pytest.mark.parametrize("block", [128, 256, 2048])
-@pytest.mark.parametrize("gdt", ["fp32", "bf16"])
+@pytest.mark.parametrize("gdt", ["fp32", "bf16", "fp16"])
 def test_efq_permuted_matches_oracle(block, gdt):
-    rng = np.random.default_rng(block + (gdt == "bf16"))
+    rng = np.random.default_rng(block + ["fp32", "bf16", "fp16"].index(gdt))
     for n_part, part in [(1, max(1024, block)), (5, max(1152, block * 3 // 2 // block * block or block)),
                          (8, max(2048, block)), (32, max(1024, block) + block)]:
         part = (part // block) * block
         n = n_part * part
         slots = [int(v) for v in rng.permutation(n_part)]
         x = grad_values(n, seed=n + block, special=True, block=block)
-        g = as_bf16_bits(x) if gdt == "bf16" else x
+        g = as_dtype(x, gdt, seed=n)
         for with_ef in (False, True):
             ef_h = grad_values(n, seed=3, std=1e-5) if with_ef else None
             ef_o = ef_h.copy() if with_ef else None
@@ -546,18 +547,18 @@ def test_hierarchical_qgz_delivers_each_rank_its_partition():
 # ------------------------------------------------- batched EF quantize --
 
 @pytest.mark.parametrize("block", [128, 256, 2048])
-@pytest.mark.parametrize("gdt", ["fp32", "bf16"])
+@pytest.mark.parametrize("gdt", ["fp32", "bf16", "fp16"])
 @pytest.mark.parametrize("with_ef", [False, True])
 def test_efq_batched_matches_oracle(block, gdt, with_ef):
-    """170 tensors (three launches of at most 80 plus their tail launches),
-    ragged lengths from 1 element to several tiles."""
-    rng = np.random.default_rng(block * 7 + (gdt == "bf16") * 3 + with_ef)
+    """170 tensors (three launches of at most 80), ragged lengths from 1
+    element to several tiles."""
+    rng = np.random.default_rng(block * 7 + ["fp32", "bf16", "fp16"].index(gdt) * 3 + with_ef)
     segs_g, exp = [], []
     for i in range(170):
         n = int(rng.choice([1, 3, block - 1, block, 1024, 4096, 4096 + 17, 3 * max(1024, block) + 5,
                             20000]))
         x = grad_values(n, seed=300 + i, special=True, block=block)
-        g = as_bf16_bits(x) if gdt == "bf16" else x
+        g = as_dtype(x, gdt, seed=i)
         ef_h = grad_values(n, seed=900 + i, std=1e-5) if with_ef else None
         ef_o = ef_h.copy() if with_ef else None
         c_o, s_o = O.quantize_ef_int4(g, ef_o, block, 0.9, 1.0)

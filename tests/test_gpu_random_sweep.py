@@ -8,7 +8,8 @@ import pytest
 import torch
 
 import oracle as O
-from tests.gpu_helpers import Guarded, as_bf16_bits, assert_bits_equal, grad_values, to_gpu, to_host
+from tests.gpu_helpers import (Guarded, as_dtype, assert_bits_equal, grad_values,
+                               to_gpu, to_host)
 from tests.test_gpu_parity import BLOCKS, Z, check_dr, check_efq, sr_inputs
 
 pytestmark = pytest.mark.gpu
@@ -31,20 +32,23 @@ def _size(rng, block):
     return max(1, int(rng.integers(1, 10)) * m + int(rng.choice([-3, -1, 0, 1, 5])))
 
 
+DTYPES = ["fp32", "bf16", "fp16"]
+
+
 @pytest.mark.parametrize("case", range(24))
 def test_efq_random_configs(case):
     rng = np.random.default_rng(1000 + case)
     block = int(rng.choice(BLOCKS))
     n = _size(rng, block)
-    bf16 = bool(rng.integers(0, 2))
+    gdt = DTYPES[int(rng.integers(0, 3))]
     with_ef = bool(rng.integers(0, 2))
     be, br = [(0.9, 1.0), (1.0, 1.0), (0.0, 1.0), (0.75, 0.25)][int(rng.integers(0, 4))]
     x = grad_values(n, seed=2000 + case, std=10.0 ** rng.uniform(-5, -1), special=True,
                     block=block)
-    g = as_bf16_bits(x) if bf16 else x
+    g = as_dtype(x, gdt, seed=case)
     ef = grad_values(n, seed=3000 + case, std=1e-5) if with_ef else None
     check_efq(g, ef, block, be, br,
-              f"random efq case={case} n={n} B={block} bf16={bf16} ef={with_ef} beta=({be},{br})")
+              f"random efq case={case} n={n} B={block} {gdt} ef={with_ef} beta=({be},{br})")
 
 
 @pytest.mark.parametrize("case", range(16))
@@ -65,24 +69,24 @@ def test_int8_random_configs(case):
     rng = np.random.default_rng(6000 + case)
     block = int(rng.choice(BLOCKS))
     n = _size(rng, block)
-    bf16 = bool(rng.integers(0, 2))
+    wdt = DTYPES[int(rng.integers(0, 3))]
     x = grad_values(n, seed=7000 + case, std=10.0 ** rng.uniform(-3, 0), special=True,
                     block=block)
-    w = as_bf16_bits(x) if bf16 else x
+    w = as_dtype(x, wdt, seed=case)
     c_o, s_o = O.quant_int8(w, block)
     codes = Guarded(n, torch.int8)
     scales = Guarded(-(-n // block), torch.float32)
     Z().zq_quant_int8(to_gpu(w), block, codes.t, scales.t)
     torch.cuda.synchronize()
-    what = f"random int8 case={case} n={n} B={block} bf16={bf16}"
+    what = f"random int8 case={case} n={n} B={block} {wdt}"
     assert_bits_equal(codes.host().view(np.uint8), c_o.view(np.uint8), what + " codes")
     assert_bits_equal(scales.host(), s_o, what + " scales")
-    out_bf16 = bool(rng.integers(0, 2))
-    o_o = O.dequant_int8(c_o, s_o, block, out_bf16=out_bf16)
-    out = Guarded(n, torch.bfloat16 if out_bf16 else torch.float32)
+    odt = DTYPES[int(rng.integers(0, 3))]
+    o_o = O.dequant_int8(c_o, s_o, block, out_bf16=odt == "bf16", out_f16=odt == "fp16")
+    out = Guarded(n, {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[odt])
     Z().zq_dequant_int8(to_gpu(c_o), to_gpu(s_o), block, out.t)
     torch.cuda.synchronize()
-    assert_bits_equal(out.host(), o_o, what + f" dequant bf16={out_bf16}")
+    assert_bits_equal(out.host(), o_o, what + f" dequant to {odt}")
 
 
 @pytest.mark.parametrize("case", range(12))

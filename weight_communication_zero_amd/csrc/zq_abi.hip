@@ -30,6 +30,12 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 size_t nblocks(size_t n, uint32_t block) { return (n + block - 1) / block; }
 
+// Element types of the data streams; the values double as zq::ElemType.
+bool known_dtype(int d) { return d == ZQ_FP32 || d == ZQ_BF16 || d == ZQ_FP16; }
+size_t dtype_bytes(int d) { return d == ZQ_FP32 ? 4 : 2; }
+static_assert(ZQ_FP32 == zq::kF32 && ZQ_BF16 == zq::kBF16 && ZQ_FP16 == zq::kF16,
+              "zq_dtype values are the kernels' element types");
+
 zq_status launched(hipError_t e) { return e == hipSuccess ? ZQ_OK : ZQ_ERR_LAUNCH; }
 
 // The integer a C caller passed for an enum parameter.  Values outside the
@@ -51,7 +57,7 @@ zq_status zq_quantize_ef_int4(const void* g, zq_dtype g_dtype_arg, float* ef, si
                               float beta_e, float beta_r, uint8_t* codes, float* scales,
                               void* stream) {
     const int g_dtype = raw_enum(g_dtype_arg);
-    if (g_dtype != ZQ_FP32 && g_dtype != ZQ_BF16)
+    if (!known_dtype(g_dtype))
         return ZQ_ERR_DTYPE;
     if (!valid_block(block))
         return ZQ_ERR_BLOCK;
@@ -63,12 +69,12 @@ zq_status zq_quantize_ef_int4(const void* g, zq_dtype g_dtype_arg, float* ef, si
         return ZQ_ERR_NULL;
     if (!aligned(g, 16) || !aligned(ef, 16) || !aligned(codes, 16) || !aligned(scales, 4))
         return ZQ_ERR_ALIGN;
-    const size_t gb = n * (g_dtype == ZQ_BF16 ? 2 : 4), eb = ef ? n * 4 : 0;
+    const size_t gb = n * dtype_bytes(g_dtype), eb = ef ? n * 4 : 0;
     const size_t cb = zq_int4_code_bytes(n), sb = nblocks(n, block) * 4;
     if (overlap(codes, cb, g, gb) || overlap(codes, cb, ef, eb) || overlap(codes, cb, scales, sb) ||
         overlap(scales, sb, g, gb) || overlap(scales, sb, ef, eb) || overlap(ef, eb, g, gb))
         return ZQ_ERR_ALIAS;
-    return launched(zq::launch_quantize_ef_int4(g, g_dtype == ZQ_BF16, ef, n, block, beta_e,
+    return launched(zq::launch_quantize_ef_int4(g, g_dtype, ef, n, block, beta_e,
                                                 beta_r, codes, scales, (hipStream_t)stream));
 }
 
@@ -77,7 +83,7 @@ zq_status zq_quantize_ef_int4_permuted(const void* g, zq_dtype g_dtype_arg, floa
                                        float* scales, uint32_t n_part,
                                        const uint32_t* slot_of_part, void* stream) {
     const int g_dtype = raw_enum(g_dtype_arg);
-    if (g_dtype != ZQ_FP32 && g_dtype != ZQ_BF16)
+    if (!known_dtype(g_dtype))
         return ZQ_ERR_DTYPE;
     if (!valid_block(block))
         return ZQ_ERR_BLOCK;
@@ -103,12 +109,12 @@ zq_status zq_quantize_ef_int4_permuted(const void* g, zq_dtype g_dtype_arg, floa
     }
     if (!aligned(g, 16) || !aligned(ef, 16) || !aligned(codes, 16) || !aligned(scales, 4))
         return ZQ_ERR_ALIGN;
-    const size_t gb = n * (g_dtype == ZQ_BF16 ? 2 : 4), eb = ef ? n * 4 : 0;
+    const size_t gb = n * dtype_bytes(g_dtype), eb = ef ? n * 4 : 0;
     const size_t cb = zq_int4_code_bytes(n), sb = nblocks(n, block) * 4;
     if (overlap(codes, cb, g, gb) || overlap(codes, cb, ef, eb) || overlap(codes, cb, scales, sb) ||
         overlap(scales, sb, g, gb) || overlap(scales, sb, ef, eb) || overlap(ef, eb, g, gb))
         return ZQ_ERR_ALIAS;
-    return launched(zq::launch_quantize_ef_int4_permuted(g, g_dtype == ZQ_BF16, ef, n, block,
+    return launched(zq::launch_quantize_ef_int4_permuted(g, g_dtype, ef, n, block,
                                                          beta_e, beta_r, codes, scales, perm,
                                                          (hipStream_t)stream));
 }
@@ -117,7 +123,7 @@ zq_status zq_quantize_ef_int4_batched(const zq_efq_segment* segs, uint32_t n_seg
                                       zq_dtype g_dtype_arg, uint32_t block, float beta_e,
                                       float beta_r, void* stream) {
     const int g_dtype = raw_enum(g_dtype_arg);
-    if (g_dtype != ZQ_FP32 && g_dtype != ZQ_BF16)
+    if (!known_dtype(g_dtype))
         return ZQ_ERR_DTYPE;
     if (!valid_block(block))
         return ZQ_ERR_BLOCK;
@@ -136,7 +142,7 @@ zq_status zq_quantize_ef_int4_batched(const zq_efq_segment* segs, uint32_t n_seg
     ranges.reserve(4 * (size_t)n_seg);
     dev.reserve(n_seg);
     int ef_state = -1;  // unknown / 0 none / 1 all
-    const size_t esz = g_dtype == ZQ_BF16 ? 2 : 4;
+    const size_t esz = dtype_bytes(g_dtype);
     for (uint32_t i = 0; i < n_seg; ++i) {
         const zq_efq_segment& s = segs[i];
         if (s.n > kMaxSegElems)
@@ -172,7 +178,7 @@ zq_status zq_quantize_ef_int4_batched(const zq_efq_segment* segs, uint32_t n_seg
             max_end_written = std::max(max_end_written, r.hi);
     }
     return launched(zq::launch_quantize_ef_int4_batched(dev.data(), (uint32_t)dev.size(),
-                                                        g_dtype == ZQ_BF16, ef_state == 1, block,
+                                                        g_dtype, ef_state == 1, block,
                                                         beta_e, beta_r, (hipStream_t)stream));
 }
 
@@ -318,7 +324,7 @@ zq_status zq_dequant_reduce_batched(const zq_dr_segment* segs, uint32_t n_seg, u
 zq_status zq_quant_int8(const void* w, zq_dtype w_dtype_arg, size_t n, uint32_t block, int8_t* codes,
                         float* scales, void* stream) {
     const int w_dtype = raw_enum(w_dtype_arg);
-    if (w_dtype != ZQ_FP32 && w_dtype != ZQ_BF16)
+    if (!known_dtype(w_dtype))
         return ZQ_ERR_DTYPE;
     if (!valid_block(block))
         return ZQ_ERR_BLOCK;
@@ -330,17 +336,17 @@ zq_status zq_quant_int8(const void* w, zq_dtype w_dtype_arg, size_t n, uint32_t 
         return ZQ_ERR_NULL;
     if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scales, 4))
         return ZQ_ERR_ALIGN;
-    const size_t wb = n * (w_dtype == ZQ_BF16 ? 2 : 4), sb = nblocks(n, block) * 4;
+    const size_t wb = n * dtype_bytes(w_dtype), sb = nblocks(n, block) * 4;
     if (overlap(codes, n, w, wb) || overlap(scales, sb, w, wb) || overlap(codes, n, scales, sb))
         return ZQ_ERR_ALIAS;
     return launched(
-        zq::launch_quant_int8(w, w_dtype == ZQ_BF16, n, block, codes, scales, (hipStream_t)stream));
+        zq::launch_quant_int8(w, w_dtype, n, block, codes, scales, (hipStream_t)stream));
 }
 
 zq_status zq_dequant_int8(const int8_t* codes, const float* scales, size_t n, uint32_t block,
                           void* out, zq_dtype out_dtype_arg, void* stream) {
     const int out_dtype = raw_enum(out_dtype_arg);
-    if (out_dtype != ZQ_FP32 && out_dtype != ZQ_BF16)
+    if (!known_dtype(out_dtype))
         return ZQ_ERR_DTYPE;
     if (!valid_block(block))
         return ZQ_ERR_BLOCK;
@@ -352,10 +358,10 @@ zq_status zq_dequant_int8(const int8_t* codes, const float* scales, size_t n, ui
         return ZQ_ERR_NULL;
     if (!aligned(codes, 16) || !aligned(scales, 4) || !aligned(out, 16))
         return ZQ_ERR_ALIGN;
-    const size_t ob = n * (out_dtype == ZQ_BF16 ? 2 : 4), sb = nblocks(n, block) * 4;
+    const size_t ob = n * dtype_bytes(out_dtype), sb = nblocks(n, block) * 4;
     if (overlap(out, ob, codes, n) || overlap(out, ob, scales, sb))
         return ZQ_ERR_ALIAS;
-    return launched(zq::launch_dequant_int8(codes, scales, n, block, out, out_dtype == ZQ_BF16,
+    return launched(zq::launch_dequant_int8(codes, scales, n, block, out, out_dtype,
                                             (hipStream_t)stream));
 }
 

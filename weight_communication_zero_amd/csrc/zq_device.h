@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "zq_launch.h"
+
 namespace zq {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -52,12 +54,57 @@ __device__ __forceinline__ float bitsf(uint32_t u) { return __builtin_bit_cast(f
 __device__ __forceinline__ float bf16lo(uint32_t w) { return bitsf(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return bitsf(w & 0xFFFF0000u); }
 
+// IEEE binary16 bit pattern -> fp32 (exact, subnormals included:
+// v_cvt_f32_f16, the high half through the operand word select).
+__device__ __forceinline__ float f16lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)w);
+}
+__device__ __forceinline__ float f16hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// Low / high 16-bit element of a word of bf16 or fp16 values, as fp32.
+template <int T>
+__device__ __forceinline__ float half_lo(uint32_t w) {
+    static_assert(T == kBF16 || T == kF16, "16-bit element types only");
+    if constexpr (T == kBF16)
+        return bf16lo(w);
+    else
+        return f16lo(w);
+}
+template <int T>
+__device__ __forceinline__ float half_hi(uint32_t w) {
+    static_assert(T == kBF16 || T == kF16, "16-bit element types only");
+    if constexpr (T == kBF16)
+        return bf16hi(w);
+    else
+        return f16hi(w);
+}
+
 // Two fp32 -> packed bf16 pair, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
 // Only used on finite values.
 __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
     typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
     bf2 v = {(__bf16)lo, (__bf16)hi};
     return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two fp32 -> packed IEEE binary16 pair, round to nearest even (the MODE
+// register's default rounding; not the round-toward-zero pkrtz form);
+// magnitudes from 65520 up become infinity, small ones fp16 subnormals.
+__device__ __forceinline__ uint32_t pack_f16_rne(float lo, float hi) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    h2 v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int T>
+__device__ __forceinline__ uint32_t pack_half_rne(float lo, float hi) {
+    static_assert(T == kBF16 || T == kF16, "16-bit element types only");
+    if constexpr (T == kBF16)
+        return pack_bf16_rne(lo, hi);
+    else
+        return pack_f16_rne(lo, hi);
 }
 
 // |x| as an unsigned bit pattern: for non-NaN values its unsigned order is

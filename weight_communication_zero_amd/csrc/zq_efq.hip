@@ -6,7 +6,8 @@
 //   c = g + e;  s = absmax(c over the block) / 7;  k = clamp(rne(c / s), +-7)
 //   e' = beta_e * e + beta_r * (c - k s)          (every step rounded in fp32)
 //
-// One pass over HBM: read g (4 or 2 B/elem) and e (4 B), write e (4 B),
+// g is fp32, bf16 or fp16 (the LoCo kernel's half loads), widened to fp32
+// exactly.  One pass over HBM: read g (4 or 2 B/elem) and e (4 B), write e (4 B),
 // codes (0.5 B) and one fp32 scale per block.  Layout on the wave: a wave
 // owns a tile of U sub-vectors of 256 elements; in sub-vector u lane l holds
 // the 4 consecutive elements starting at u*256 + 4l, so every load and store
@@ -59,7 +60,7 @@ __device__ __forceinline__ PermMap perm_map(const PartPerm& pp, size_t base) {
     return m;
 }
 
-template <bool BF16, bool EF, int B, bool MASK, class Map = IdentityMap>
+template <int IN, bool EF, int B, bool MASK, class Map = IdentityMap>
 __device__ __forceinline__ void efq_tile(const void* __restrict__ gv, float* __restrict__ ef,
                                          size_t n, float beta_e, float beta_r,
                                          uint8_t* __restrict__ codes, float* __restrict__ scales,
@@ -76,12 +77,12 @@ __device__ __forceinline__ void efq_tile(const void* __restrict__ gv, float* __r
         const size_t i0 = base + (size_t)u * G::SUB + (size_t)lane * 4;
         float gv4[4];
         if constexpr (!MASK) {
-            if constexpr (BF16) {
+            if constexpr (IN != kF32) {
                 u2 w = ld_stream((const u2*)((const uint16_t*)gv + i0));
-                gv4[0] = bf16lo(w.x);
-                gv4[1] = bf16hi(w.x);
-                gv4[2] = bf16lo(w.y);
-                gv4[3] = bf16hi(w.y);
+                gv4[0] = half_lo<IN>(w.x);
+                gv4[1] = half_hi<IN>(w.x);
+                gv4[2] = half_lo<IN>(w.y);
+                gv4[3] = half_hi<IN>(w.y);
             } else {
                 f4 w = ld_stream((const f4*)((const float*)gv + i0));
                 gv4[0] = w.x;
@@ -100,8 +101,8 @@ __device__ __forceinline__ void efq_tile(const void* __restrict__ gv, float* __r
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const bool in = i0 + j < n;
-                if constexpr (BF16)
-                    gv4[j] = in ? bf16lo(((const uint16_t*)gv)[i0 + j]) : 0.0f;
+                if constexpr (IN != kF32)
+                    gv4[j] = in ? half_lo<IN>(((const uint16_t*)gv)[i0 + j]) : 0.0f;
                 else
                     gv4[j] = in ? ((const float*)gv)[i0 + j] : 0.0f;
                 if constexpr (EF)
@@ -210,7 +211,7 @@ __device__ __forceinline__ void efq_tile(const void* __restrict__ gv, float* __r
 // multiple of the tile) goes, in the same launch, to the one wave whose loop
 // stops exactly at it.  The two paths run one after the other, so their
 // registers are not live at once.
-template <bool BF16, bool EF, int B>
+template <int IN, bool EF, int B>
 __global__ __launch_bounds__(kBlockThreads) void efq_kernel(const void* __restrict__ g,
                                                             float* __restrict__ ef, size_t n,
                                                             float beta_e, float beta_r,
@@ -220,24 +221,24 @@ __global__ __launch_bounds__(kBlockThreads) void efq_kernel(const void* __restri
     const size_t nfull = n / G::TILE;
     size_t t = stream_wave_id<kGeomStream.threads>();
     for (; t < nfull; t += wave_count())
-        efq_tile<BF16, EF, B, false>(g, ef, n, beta_e, beta_r, codes, scales, t);
+        efq_tile<IN, EF, B, false>(g, ef, n, beta_e, beta_r, codes, scales, t);
     if (t == nfull && n % G::TILE)
-        efq_tile<BF16, EF, B, true>(g, ef, n, beta_e, beta_r, codes, scales, t);
+        efq_tile<IN, EF, B, true>(g, ef, n, beta_e, beta_r, codes, scales, t);
 }
 
-template <bool BF16, bool EF, int B>
+template <int IN, bool EF, int B>
 hipError_t launch_b(const void* g, float* ef, size_t n, float beta_e, float beta_r,
                     uint8_t* codes, float* scales, hipStream_t stream) {
     using G = EfqGeom<B>;
     const size_t ntiles = (n + G::TILE - 1) / G::TILE;
     void* args[] = {(void*)&g, (void*)&ef, (void*)&n, (void*)&beta_e, (void*)&beta_r,
                     (void*)&codes, (void*)&scales};
-    return hipLaunchKernel((const void*)&efq_kernel<BF16, EF, B>,
+    return hipLaunchKernel((const void*)&efq_kernel<IN, EF, B>,
                            grid_for_tiles(ntiles, kGeomStream), dim3(kGeomStream.threads), args, 0,
                            stream);
 }
 
-template <bool BF16, bool EF, int B>
+template <int IN, bool EF, int B>
 __global__ __launch_bounds__(kBlockThreads) void efq_perm_kernel(const void* __restrict__ g,
                                                                  float* __restrict__ ef, size_t n,
                                                                  float beta_e, float beta_r,
@@ -248,14 +249,14 @@ __global__ __launch_bounds__(kBlockThreads) void efq_perm_kernel(const void* __r
     const size_t nfull = n / G::TILE;
     size_t t = stream_wave_id<kGeomStream.threads>();
     for (; t < nfull; t += wave_count())
-        efq_tile<BF16, EF, B, false>(g, ef, n, beta_e, beta_r, codes, scales, t,
+        efq_tile<IN, EF, B, false>(g, ef, n, beta_e, beta_r, codes, scales, t,
                                      perm_map(perm, t * G::TILE));
     if (t == nfull && n % G::TILE)
-        efq_tile<BF16, EF, B, true>(g, ef, n, beta_e, beta_r, codes, scales, t,
+        efq_tile<IN, EF, B, true>(g, ef, n, beta_e, beta_r, codes, scales, t,
                                     perm_map(perm, t * G::TILE));
 }
 
-template <bool BF16, bool EF, int B>
+template <int IN, bool EF, int B>
 hipError_t launch_perm_b(const void* g, float* ef, size_t n, float beta_e, float beta_r,
                          uint8_t* codes, float* scales, const PartPerm& perm, hipStream_t stream) {
     using G = EfqGeom<B>;
@@ -263,23 +264,23 @@ hipError_t launch_perm_b(const void* g, float* ef, size_t n, float beta_e, float
     PartPerm arg = perm;
     void* args[] = {(void*)&g, (void*)&ef, (void*)&n, (void*)&beta_e, (void*)&beta_r,
                     (void*)&codes, (void*)&scales, (void*)&arg};
-    return hipLaunchKernel((const void*)&efq_perm_kernel<BF16, EF, B>,
+    return hipLaunchKernel((const void*)&efq_perm_kernel<IN, EF, B>,
                            grid_for_tiles(ntiles, kGeomStream), dim3(kGeomStream.threads), args, 0,
                            stream);
 }
 
-template <bool BF16, bool EF>
+template <int IN, bool EF>
 hipError_t launch_perm_t(const void* g, float* ef, size_t n, uint32_t block, float be, float br,
                          uint8_t* codes, float* scales, const PartPerm& pp, hipStream_t st) {
     switch (block) {
-        case 32: return launch_perm_b<BF16, EF, 32>(g, ef, n, be, br, codes, scales, pp, st);
-        case 64: return launch_perm_b<BF16, EF, 64>(g, ef, n, be, br, codes, scales, pp, st);
-        case 128: return launch_perm_b<BF16, EF, 128>(g, ef, n, be, br, codes, scales, pp, st);
-        case 256: return launch_perm_b<BF16, EF, 256>(g, ef, n, be, br, codes, scales, pp, st);
-        case 512: return launch_perm_b<BF16, EF, 512>(g, ef, n, be, br, codes, scales, pp, st);
-        case 1024: return launch_perm_b<BF16, EF, 1024>(g, ef, n, be, br, codes, scales, pp, st);
-        case 2048: return launch_perm_b<BF16, EF, 2048>(g, ef, n, be, br, codes, scales, pp, st);
-        case 4096: return launch_perm_b<BF16, EF, 4096>(g, ef, n, be, br, codes, scales, pp, st);
+        case 32: return launch_perm_b<IN, EF, 32>(g, ef, n, be, br, codes, scales, pp, st);
+        case 64: return launch_perm_b<IN, EF, 64>(g, ef, n, be, br, codes, scales, pp, st);
+        case 128: return launch_perm_b<IN, EF, 128>(g, ef, n, be, br, codes, scales, pp, st);
+        case 256: return launch_perm_b<IN, EF, 256>(g, ef, n, be, br, codes, scales, pp, st);
+        case 512: return launch_perm_b<IN, EF, 512>(g, ef, n, be, br, codes, scales, pp, st);
+        case 1024: return launch_perm_b<IN, EF, 1024>(g, ef, n, be, br, codes, scales, pp, st);
+        case 2048: return launch_perm_b<IN, EF, 2048>(g, ef, n, be, br, codes, scales, pp, st);
+        case 4096: return launch_perm_b<IN, EF, 4096>(g, ef, n, be, br, codes, scales, pp, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -318,7 +319,7 @@ __device__ __forceinline__ uint32_t find_segment(const EfqBatch& b, uint32_t t) 
     return lo;
 }
 
-template <bool BF16, bool EF, int B>
+template <int IN, bool EF, int B>
 __global__ __launch_bounds__(kBlockThreads) void efq_batched_kernel(EfqBatch b) {
     using G = EfqGeom<B>;
     size_t ts = stream_wave_id<kGeomStream.threads>();
@@ -327,16 +328,16 @@ __global__ __launch_bounds__(kBlockThreads) void efq_batched_kernel(EfqBatch b) 
         const uint32_t s = find_segment(b, t);
         const EfqSegment& g = b.seg[s];
         const size_t local = t - (s ? b.tile_end[s - 1] : 0u);
-        efq_tile<BF16, EF, B, false>(g.g, g.ef, g.n, b.beta_e, b.beta_r, g.codes, g.scales, local);
+        efq_tile<IN, EF, B, false>(g.g, g.ef, g.n, b.beta_e, b.beta_r, g.codes, g.scales, local);
     }
     for (; ts < b.total; ts += wave_count()) {
         const EfqSegment& g = b.seg[b.tail_seg[ts - b.full]];
-        efq_tile<BF16, EF, B, true>(g.g, g.ef, g.n, b.beta_e, b.beta_r, g.codes, g.scales,
+        efq_tile<IN, EF, B, true>(g.g, g.ef, g.n, b.beta_e, b.beta_r, g.codes, g.scales,
                                     g.n / G::TILE);
     }
 }
 
-template <bool BF16, bool EF, int B>
+template <int IN, bool EF, int B>
 hipError_t launch_batched_b(const EfqSegment* segs, uint32_t n_seg, float be, float br,
                             hipStream_t stream) {
     using G = EfqGeom<B>;
@@ -371,7 +372,7 @@ hipError_t launch_batched_b(const EfqSegment* segs, uint32_t n_seg, float be, fl
         bt.total = (uint32_t)tiles;
         void* args[] = {(void*)&bt};
         const hipError_t e =
-            hipLaunchKernel((const void*)&efq_batched_kernel<BF16, EF, B>,
+            hipLaunchKernel((const void*)&efq_batched_kernel<IN, EF, B>,
                             grid_for_tiles(tiles, kGeomStream), dim3(kGeomStream.threads), args, 0,
                             stream);
         if (e != hipSuccess)
@@ -380,73 +381,97 @@ hipError_t launch_batched_b(const EfqSegment* segs, uint32_t n_seg, float be, fl
     return hipSuccess;
 }
 
-template <bool BF16, bool EF>
+template <int IN, bool EF>
 hipError_t launch_batched_t(const EfqSegment* segs, uint32_t n_seg, uint32_t block, float be,
                             float br, hipStream_t st) {
     switch (block) {
-        case 32: return launch_batched_b<BF16, EF, 32>(segs, n_seg, be, br, st);
-        case 64: return launch_batched_b<BF16, EF, 64>(segs, n_seg, be, br, st);
-        case 128: return launch_batched_b<BF16, EF, 128>(segs, n_seg, be, br, st);
-        case 256: return launch_batched_b<BF16, EF, 256>(segs, n_seg, be, br, st);
-        case 512: return launch_batched_b<BF16, EF, 512>(segs, n_seg, be, br, st);
-        case 1024: return launch_batched_b<BF16, EF, 1024>(segs, n_seg, be, br, st);
-        case 2048: return launch_batched_b<BF16, EF, 2048>(segs, n_seg, be, br, st);
-        case 4096: return launch_batched_b<BF16, EF, 4096>(segs, n_seg, be, br, st);
+        case 32: return launch_batched_b<IN, EF, 32>(segs, n_seg, be, br, st);
+        case 64: return launch_batched_b<IN, EF, 64>(segs, n_seg, be, br, st);
+        case 128: return launch_batched_b<IN, EF, 128>(segs, n_seg, be, br, st);
+        case 256: return launch_batched_b<IN, EF, 256>(segs, n_seg, be, br, st);
+        case 512: return launch_batched_b<IN, EF, 512>(segs, n_seg, be, br, st);
+        case 1024: return launch_batched_b<IN, EF, 1024>(segs, n_seg, be, br, st);
+        case 2048: return launch_batched_b<IN, EF, 2048>(segs, n_seg, be, br, st);
+        case 4096: return launch_batched_b<IN, EF, 4096>(segs, n_seg, be, br, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <bool BF16, bool EF>
+template <int IN, bool EF>
 hipError_t launch_t(const void* g, float* ef, size_t n, uint32_t block, float be, float br,
                     uint8_t* codes, float* scales, hipStream_t st) {
     switch (block) {
-        case 32: return launch_b<BF16, EF, 32>(g, ef, n, be, br, codes, scales, st);
-        case 64: return launch_b<BF16, EF, 64>(g, ef, n, be, br, codes, scales, st);
-        case 128: return launch_b<BF16, EF, 128>(g, ef, n, be, br, codes, scales, st);
-        case 256: return launch_b<BF16, EF, 256>(g, ef, n, be, br, codes, scales, st);
-        case 512: return launch_b<BF16, EF, 512>(g, ef, n, be, br, codes, scales, st);
-        case 1024: return launch_b<BF16, EF, 1024>(g, ef, n, be, br, codes, scales, st);
-        case 2048: return launch_b<BF16, EF, 2048>(g, ef, n, be, br, codes, scales, st);
-        case 4096: return launch_b<BF16, EF, 4096>(g, ef, n, be, br, codes, scales, st);
+        case 32: return launch_b<IN, EF, 32>(g, ef, n, be, br, codes, scales, st);
+        case 64: return launch_b<IN, EF, 64>(g, ef, n, be, br, codes, scales, st);
+        case 128: return launch_b<IN, EF, 128>(g, ef, n, be, br, codes, scales, st);
+        case 256: return launch_b<IN, EF, 256>(g, ef, n, be, br, codes, scales, st);
+        case 512: return launch_b<IN, EF, 512>(g, ef, n, be, br, codes, scales, st);
+        case 1024: return launch_b<IN, EF, 1024>(g, ef, n, be, br, codes, scales, st);
+        case 2048: return launch_b<IN, EF, 2048>(g, ef, n, be, br, codes, scales, st);
+        case 4096: return launch_b<IN, EF, 4096>(g, ef, n, be, br, codes, scales, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <bool EF>
+hipError_t launch_typed(const void* g, int g_type, float* ef, size_t n, uint32_t block, float be,
+                        float br, uint8_t* codes, float* scales, hipStream_t st) {
+    switch (g_type) {
+        case kF32: return launch_t<kF32, EF>(g, ef, n, block, be, br, codes, scales, st);
+        case kBF16: return launch_t<kBF16, EF>(g, ef, n, block, be, br, codes, scales, st);
+        case kF16: return launch_t<kF16, EF>(g, ef, n, block, be, br, codes, scales, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <bool EF>
+hipError_t launch_batched_typed(const EfqSegment* segs, uint32_t n_seg, int g_type, uint32_t block,
+                                float be, float br, hipStream_t st) {
+    switch (g_type) {
+        case kF32: return launch_batched_t<kF32, EF>(segs, n_seg, block, be, br, st);
+        case kBF16: return launch_batched_t<kBF16, EF>(segs, n_seg, block, be, br, st);
+        case kF16: return launch_batched_t<kF16, EF>(segs, n_seg, block, be, br, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <bool EF>
+hipError_t launch_perm_typed(const void* g, int g_type, float* ef, size_t n, uint32_t block,
+                             float be, float br, uint8_t* codes, float* scales,
+                             const PartPerm& perm, hipStream_t st) {
+    switch (g_type) {
+        case kF32: return launch_perm_t<kF32, EF>(g, ef, n, block, be, br, codes, scales, perm, st);
+        case kBF16:
+            return launch_perm_t<kBF16, EF>(g, ef, n, block, be, br, codes, scales, perm, st);
+        case kF16: return launch_perm_t<kF16, EF>(g, ef, n, block, be, br, codes, scales, perm, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_quantize_ef_int4(const void* g, bool g_bf16, float* ef, size_t n, uint32_t block,
+hipError_t launch_quantize_ef_int4(const void* g, int g_type, float* ef, size_t n, uint32_t block,
                                    float beta_e, float beta_r, uint8_t* codes, float* scales,
                                    hipStream_t stream) {
-    if (g_bf16)
-        return ef ? launch_t<true, true>(g, ef, n, block, beta_e, beta_r, codes, scales, stream)
-                  : launch_t<true, false>(g, ef, n, block, beta_e, beta_r, codes, scales, stream);
-    return ef ? launch_t<false, true>(g, ef, n, block, beta_e, beta_r, codes, scales, stream)
-              : launch_t<false, false>(g, ef, n, block, beta_e, beta_r, codes, scales, stream);
+    return ef ? launch_typed<true>(g, g_type, ef, n, block, beta_e, beta_r, codes, scales, stream)
+              : launch_typed<false>(g, g_type, ef, n, block, beta_e, beta_r, codes, scales, stream);
 }
 
-hipError_t launch_quantize_ef_int4_batched(const EfqSegment* segs, uint32_t n_seg, bool g_bf16,
+hipError_t launch_quantize_ef_int4_batched(const EfqSegment* segs, uint32_t n_seg, int g_type,
                                            bool with_ef, uint32_t block, float beta_e,
                                            float beta_r, hipStream_t stream) {
-    if (g_bf16)
-        return with_ef ? launch_batched_t<true, true>(segs, n_seg, block, beta_e, beta_r, stream)
-                       : launch_batched_t<true, false>(segs, n_seg, block, beta_e, beta_r, stream);
-    return with_ef ? launch_batched_t<false, true>(segs, n_seg, block, beta_e, beta_r, stream)
-                   : launch_batched_t<false, false>(segs, n_seg, block, beta_e, beta_r, stream);
+    return with_ef ? launch_batched_typed<true>(segs, n_seg, g_type, block, beta_e, beta_r, stream)
+                   : launch_batched_typed<false>(segs, n_seg, g_type, block, beta_e, beta_r, stream);
 }
 
-hipError_t launch_quantize_ef_int4_permuted(const void* g, bool g_bf16, float* ef, size_t n,
+hipError_t launch_quantize_ef_int4_permuted(const void* g, int g_type, float* ef, size_t n,
                                             uint32_t block, float beta_e, float beta_r,
                                             uint8_t* codes, float* scales, const PartPerm& perm,
                                             hipStream_t stream) {
-    if (g_bf16)
-        return ef ? launch_perm_t<true, true>(g, ef, n, block, beta_e, beta_r, codes, scales, perm,
-                                              stream)
-                  : launch_perm_t<true, false>(g, ef, n, block, beta_e, beta_r, codes, scales,
-                                               perm, stream);
-    return ef ? launch_perm_t<false, true>(g, ef, n, block, beta_e, beta_r, codes, scales, perm,
-                                           stream)
-              : launch_perm_t<false, false>(g, ef, n, block, beta_e, beta_r, codes, scales, perm,
-                                            stream);
+    return ef ? launch_perm_typed<true>(g, g_type, ef, n, block, beta_e, beta_r, codes, scales,
+                                        perm, stream)
+              : launch_perm_typed<false>(g, g_type, ef, n, block, beta_e, beta_r, codes, scales,
+                                         perm, stream);
 }
 
 }  // namespace zq

@@ -11,6 +11,9 @@ namespace zq {
 
 constexpr uint32_t kMaxPeers = 16;
 
+// Element types of the 16- and 32-bit data streams (the values of zq_dtype).
+enum ElemType : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
+
 // Launch geometry of a streaming kernel: threads per workgroup (64..256)
 // and the most workgroups one launch may have; a larger job walks its tiles
 // with a grid stride.  Measured on MI355X: one-tile-per-wave grids of 1-wave
@@ -49,7 +52,8 @@ inline dim3 grid_for_tiles(size_t tiles, Geometry g) {
     return dim3((uint32_t)wgs);
 }
 
-hipError_t launch_quantize_ef_int4(const void* g, bool g_bf16, float* ef, size_t n, uint32_t block,
+// g_type, w_type, out_type: an ElemType (kF32, kBF16, kF16).
+hipError_t launch_quantize_ef_int4(const void* g, int g_type, float* ef, size_t n, uint32_t block,
                                    float beta_e, float beta_r, uint8_t* codes, float* scales,
                                    hipStream_t stream);
 
@@ -62,7 +66,7 @@ struct PartPerm {
     uint32_t slot[kMaxParts];
 };
 
-hipError_t launch_quantize_ef_int4_permuted(const void* g, bool g_bf16, float* ef, size_t n,
+hipError_t launch_quantize_ef_int4_permuted(const void* g, int g_type, float* ef, size_t n,
                                             uint32_t block, float beta_e, float beta_r,
                                             uint8_t* codes, float* scales, const PartPerm& perm,
                                             hipStream_t stream);
@@ -76,7 +80,7 @@ struct EfqSegment {
     uint64_t n;
 };
 
-hipError_t launch_quantize_ef_int4_batched(const EfqSegment* segs, uint32_t n_seg, bool g_bf16,
+hipError_t launch_quantize_ef_int4_batched(const EfqSegment* segs, uint32_t n_seg, int g_type,
                                            bool with_ef, uint32_t block, float beta_e,
                                            float beta_r, hipStream_t stream);
 
@@ -126,11 +130,11 @@ struct DrBatchArgs {
 hipError_t launch_dequant_reduce_batched(const DrSegment* segs, uint32_t n_seg,
                                          const DrBatchArgs& a, uint32_t block, hipStream_t stream);
 
-hipError_t launch_quant_int8(const void* w, bool w_bf16, size_t n, uint32_t block, int8_t* codes,
+hipError_t launch_quant_int8(const void* w, int w_type, size_t n, uint32_t block, int8_t* codes,
                              float* scales, hipStream_t stream);
 
 hipError_t launch_dequant_int8(const int8_t* codes, const float* scales, size_t n, uint32_t block,
-                               void* out, bool out_bf16, hipStream_t stream);
+                               void* out, int out_type, hipStream_t stream);
 
 hipError_t launch_sr_accumulate(uint16_t* dst, uint16_t* src, size_t n, uint64_t seed,
                                 uint64_t counter_base, bool zero_src, hipStream_t stream);

@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("ZQ_LIB") or os.path.join(_HERE, "libzq.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "zq.h")
 
-ZQ_FP32, ZQ_BF16 = 0, 1
+ZQ_FP32, ZQ_BF16, ZQ_FP16 = 0, 1, 2
 
 STATUS = {
     0: "ZQ_OK", 1: "ZQ_ERR_NULL", 2: "ZQ_ERR_SIZE", 3: "ZQ_ERR_BLOCK", 4: "ZQ_ERR_ALIGN",
@@ -128,6 +128,8 @@ def _dtype(t) -> int:
         return ZQ_FP32
     if t.dtype == torch.bfloat16:
         return ZQ_BF16
+    if t.dtype == torch.float16:
+        return ZQ_FP16
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -149,7 +151,7 @@ def _need(name: str, t, numel: int, dtypes) -> None:
 
 _F32 = (torch.float32,)
 _BF16 = (torch.bfloat16,)
-_FLOAT = (torch.float32, torch.bfloat16)
+_FLOAT = (torch.float32, torch.bfloat16, torch.float16)
 _U8 = (torch.uint8,)
 _I8 = (torch.int8,)
 
@@ -169,7 +171,7 @@ def num_blocks(n: int, block: int) -> int:
 
 def zq_quantize_ef_int4(g, ef, block: int, beta_e: float, beta_r: float, codes, scales,
                         stream=None, n: int | None = None) -> None:
-    """EF int4 quantize: g (fp32/bf16), ef (fp32 or None, updated in place)
+    """EF int4 quantize: g (fp32/bf16/fp16), ef (fp32 or None, updated in place)
     -> codes (uint8, ceil(n/2)), scales (fp32, ceil(n/block))."""
     n = g.numel() if n is None else n
     nb = (n + block - 1) // block if block > 0 else 0
