@@ -233,13 +233,14 @@ def test_int8_weights_0p85b_sampled_blocks(wdt):
 # ------------------------------------------- qgZ + LoCo: 0.85B and 7.5B --
 
 def run_two_level(tensors, tag, steps, levels, n_sample, seed, beta=(0.9, 1.0), rq_beta=None,
-                  reset_every=None):
+                  reset_every=None, gdt=torch.float32):
     """EF quantize of the whole gradient, then level-1 reduce over P1 chunks
     (with requant when there is a second level), then level-2 reduce over P2
     sub-chunks; sampled blocks checked at every step.  LoCo variants: `beta`
     = (beta_e, beta_r) of the EF update, `rq_beta` turns on an EF buffer at
     the requant (the per-parameter inter-level EF buffer), `reset_every`
-    zeroes the EF buffers every that many steps."""
+    zeroes the EF buffers every that many steps, `gdt` is the gradient's
+    dtype."""
     M = synth.total(tensors)
     B = 128
     P1 = 8
@@ -256,7 +257,7 @@ def run_two_level(tensors, tag, steps, levels, n_sample, seed, beta=(0.9, 1.0), 
     L1 = (np.arange(P2)[:, None] * nb2 + S[None, :]).reshape(-1) if two else S  # level-1 blocks
     L0 = (np.arange(P1)[:, None] * nb1 + L1[None, :]).reshape(-1)  # EF-quantize blocks
 
-    g = torch.empty(M, dtype=torch.float32, device="cuda")
+    g = torch.empty(M, dtype=gdt, device="cuda")
     ef = torch.zeros(M, dtype=torch.float32, device="cuda")
     codes = torch.empty(M // 2, dtype=torch.uint8, device="cuda")
     scales = torch.empty(M // B, dtype=torch.float32, device="cuda")
@@ -349,6 +350,13 @@ def test_loco_requant_ef_7p5b_two_level_sampled():
     """LoCo variant: an EF buffer at the intra-node requant as well (beta 0.9)."""
     run_two_level(synth.llama_7p5b(), "llama7p5b", steps=3, levels=2, n_sample=16, seed=6,
                   rq_beta=(0.9, 1.0))
+
+
+def test_qgz_loco_0p85b_fp16_gradients_sampled():
+    """fp16 gradients (the LoCo kernel's half loads) through the whole step
+    at full size, past the XCD-ordered workgroup map."""
+    run_two_level(synth.llama_0p85b(), "llama0p85b", steps=3, levels=1, n_sample=48, seed=8,
+                  gdt=torch.float16)
 
 
 def test_loco_moving_average_with_reset_0p85b_sampled():
