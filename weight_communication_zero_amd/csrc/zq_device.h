@@ -297,4 +297,31 @@ __device__ __forceinline__ size_t stream_wave_id() {
 }
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
+// Segment lookup of the batched kernels.  `ends` holds the segments'
+// cumulative tile counts (non-decreasing; entries from nseg on are ignored),
+// and the segment of tile t is the number of entries <= t.  Lane k keeps
+// entries k and k + 64 in registers, so a lookup is one or two vector
+// compares and the population counts of their ballots: a few instructions
+// instead of a chain of dependent scalar loads (binary search) or a scalar
+// compare per entry (scan), both of which load the compute unit's one scalar
+// ALU on every tile.
+template <int N>
+struct SegmentFinder {
+    uint32_t e0, e1;
+    __device__ __forceinline__ SegmentFinder(const uint32_t (&ends)[N], uint32_t nseg) {
+        const uint32_t lane = (uint32_t)lane_id();
+        e0 = lane < nseg ? ends[lane] : UINT32_MAX;
+        e1 = UINT32_MAX;
+        if constexpr (N > kWave)
+            e1 = lane + kWave < nseg ? ends[lane + kWave] : UINT32_MAX;
+    }
+    __device__ __forceinline__ uint32_t operator()(uint32_t t) const {
+        static_assert(N <= 2 * kWave, "two table entries per lane at most");
+        uint32_t s = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(t >= e0));
+        if constexpr (N > kWave)
+            s += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(t >= e1));
+        return s;
+    }
+};
+
 }  // namespace zq

@@ -744,9 +744,9 @@ hipError_t launch_peers(const DrParams& p, hipStream_t st) {
 // review thread: the LoCo path reduces parameter by parameter, each with its
 // own requant error-feedback buffer).  A launch takes up to kDrSegs segments
 // (the table rides in the kernel arguments) and runs all of their tiles:
-// first the full ones, a wave finding its segment by binary search over the
-// cumulative full-tile counts, then the ragged last tiles, the k-th of which
-// belongs to segment tail_seg[k].
+// first the full ones, a wave finding its segment from the cumulative
+// full-tile counts (SegmentFinder), then the ragged last tiles, the k-th of
+// which belongs to segment tail_seg[k].
 #ifndef ZQ_DR_SEGS
 #define ZQ_DR_SEGS 48
 #endif
@@ -782,25 +782,14 @@ struct DrSegView {
     __device__ const float* scales_of(uint32_t q) const { return scales + q * sstride; }
 };
 
-__device__ __forceinline__ uint32_t find_dr_segment(const DrBatch& b, uint32_t t) {
-    uint32_t lo = 0, hi = b.nseg - 1;  // first s with t < tile_end[s]
-    while (lo < hi) {
-        const uint32_t mid = (lo + hi) >> 1;
-        if (t < b.tile_end[mid])
-            hi = mid;
-        else
-            lo = mid + 1;
-    }
-    return lo;
-}
-
 template <int B, int PMAX, bool OUT, bool RQ, bool EF>
 __global__ __launch_bounds__(kBlockThreads) void dr_batched_kernel(DrBatch b) {
     using G = DrGeomOf<B, RQ, EF>;
+    const SegmentFinder<kDrSegs> find(b.tile_end, b.nseg);
     size_t ts = wave_id();
     for (; ts < b.full; ts += wave_count()) {
         const uint32_t t = (uint32_t)ts;
-        const uint32_t s = find_dr_segment(b, t);
+        const uint32_t s = find(t);
         const DrSegment& g = b.seg[s];
         const DrSegView v = {g.codes,    g.scales,    g.codes_stride, g.scales_stride, b.P,
                              g.n,        b.alpha,     g.out,          g.rq_codes,      g.rq_scales,

@@ -286,8 +286,8 @@ hipError_t launch_perm_t(const void* g, float* ef, size_t n, uint32_t block, flo
 }
 
 // Batched segments.  One launch runs every tile of up to kEfqSegs segments:
-// first all full tiles (a wave finds its segment by binary search over the
-// cumulative full-tile counts in the kernel arguments, seven scalar loads),
+// first all full tiles (a wave finds its segment from the cumulative
+// full-tile counts in the kernel arguments, held one per lane: SegmentFinder),
 // then the ragged last tiles, the k-th of which belongs to segment
 // tail_seg[k].  80 segments (3.6 KB of kernel arguments) take the 7.5B
 // model's 327 tensors in 5 launches.
@@ -307,25 +307,14 @@ struct EfqBatch {
 };
 static_assert(kEfqSegs <= 256, "tail_seg holds 8-bit segment indices");
 
-__device__ __forceinline__ uint32_t find_segment(const EfqBatch& b, uint32_t t) {
-    uint32_t lo = 0, hi = b.nseg - 1;  // first s with t < tile_end[s]
-    while (lo < hi) {
-        const uint32_t mid = (lo + hi) >> 1;
-        if (t < b.tile_end[mid])
-            hi = mid;
-        else
-            lo = mid + 1;
-    }
-    return lo;
-}
-
 template <int IN, bool EF, int B>
 __global__ __launch_bounds__(kBlockThreads) void efq_batched_kernel(EfqBatch b) {
     using G = EfqGeom<B>;
+    const SegmentFinder<kEfqSegs> find(b.tile_end, b.nseg);
     size_t ts = stream_wave_id<kGeomStream.threads>();
     for (; ts < b.full; ts += wave_count()) {
         const uint32_t t = (uint32_t)ts;
-        const uint32_t s = find_segment(b, t);
+        const uint32_t s = find(t);
         const EfqSegment& g = b.seg[s];
         const size_t local = t - (s ? b.tile_end[s - 1] : 0u);
         efq_tile<IN, EF, B, false>(g.g, g.ef, g.n, b.beta_e, b.beta_r, g.codes, g.scales, local);

@@ -238,15 +238,12 @@ __device__ __forceinline__ void zero_seg_tile(const SrSegment& g, uint64_t local
 }
 
 __global__ __launch_bounds__(kBlockThreads) void sr_batched_kernel(SrBatch b) {
+    // Segment of tile t: the number of cumulative counts it has passed (a
+    // scalar compare per entry measured 6 % slower on GPT-2's 148 tensors).
+    const SegmentFinder<kSegsPerLaunch> find(b.tile_end, (uint32_t)kSegsPerLaunch);
     for (size_t ts = stream_wave_id<kGeomStream.threads>(); ts < b.total; ts += wave_count()) {
         const uint32_t t = (uint32_t)ts;
-        // Segment of tile t: the number of cumulative counts it has passed.
-        // Independent compares against table entries the compiler loads once,
-        // not a chain of dependent loads.
-        uint32_t s = 0;
-#pragma unroll
-        for (int k = 0; k < kSegsPerLaunch - 1; ++k)
-            s += t >= b.tile_end[k] ? 1u : 0u;
+        const uint32_t s = find(t);
         const uint32_t local = t - (s ? b.tile_end[s - 1] : 0u);
         if (local < b.sr_tiles[s])
             sr_seg_tile(b.seg[s], local, b.zero != 0);
