@@ -277,3 +277,43 @@ def test_dequant_reduce_batched_validation():
     # two segments writing the same output
     assert call([a, Seg(FAKE + 0x1000000, FAKE + 0x1100000, 2048, 32, 4096, FAKE + 0x200000, None,
                         None, None)]) == zq.ZQ_ERR_ALIAS
+
+
+def test_header_is_c99_and_the_library_links_from_c(tmp_path):
+    """include/zq.h is plain C: a C99 program (-pedantic -Werror) includes it,
+    links libzq.so and calls the host-only entry points (no GPU is touched)."""
+    import os
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    src = tmp_path / "use_zq.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <string.h>
+#include "zq.h"
+int main(void) {
+    uint32_t slot[8];
+    if (zq_zeropp_slots(4, 2, slot) != 8) return 1;
+    /* rank node*4 + local sits in slot local*2 + node */
+    if (slot[1] != 2 || slot[4] != 1 || slot[7] != 7) return 2;
+    if (zq_int4_code_bytes(7) != 4 || zq_num_blocks(1000, 128) != 8) return 3;
+    if (strcmp(zq_status_str(ZQ_ERR_ALIGN), zq_status_str(ZQ_OK)) == 0) return 4;
+    /* a refused call enqueues nothing and needs no device */
+    if (zq_quantize_ef_int4(NULL, ZQ_FP16, NULL, 16, 128, 1.0f, 1.0f, NULL, NULL, NULL) !=
+        ZQ_ERR_NULL) return 5;
+    puts("ok");
+    return 0;
+}
+''')
+    exe = tmp_path / "use_zq"
+    lib = os.path.join(root, "weight_communication_zero_amd", "libzq.so")
+    r = subprocess.run([gcc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror",
+                        "-I", os.path.join(root, "include"), str(src), lib,
+                        "-Wl,-rpath," + os.path.dirname(lib), "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
