@@ -10,9 +10,10 @@
 //
 // One pass: P * (0.5 B + 4/B B) read per output element, 4 B written when
 // out is requested, 0.5 B + 4/B B (+8 B with requant EF) for the requant.
-// In sub-vector u lane l owns the 8 outputs starting at u*512 + 8l, i.e. one
-// 32-bit word of codes per peer: each code load instruction of the wave
-// reads 256 contiguous bytes.  The sum order is fixed (ascending peer), so
+// In sub-vector u lane l owns the VEC outputs starting at u*64*VEC + VEC*l:
+// VEC = 8 for the requant without EF (one 32-bit word of codes per peer, so
+// each code load instruction of the wave reads 256 contiguous bytes), 4 for
+// the fp32-out reduce and the requant with EF.  The sum order is fixed (ascending peer), so
 // the fp32 sums -- and the requant codes that depend on their exact bits --
 // are deterministic.  No LDS.
 #pragma once
