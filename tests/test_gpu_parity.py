@@ -640,6 +640,33 @@ def test_requant_exact_ties(with_rq_ef):
         assert_bits_equal(to_host(rq_ef), rq_ef_o, what + " rq_ef")
 
 
+@pytest.mark.parametrize("P,block", [(8, 128), (5, 256)])
+def test_requant_several_tiles_per_wave(P, block):
+    """The requant without EF runs a fixed grid of 16,384 waves that walk
+    the tiles with a stride of the wave count, so only chunks above 16,384
+    tiles give a wave more than one: here about 2^25 outputs (two to four
+    tiles per wave, depending on the tile length), an odd length with a
+    ragged last tile.  Raw nibbles (-8 included) with positive scales keep
+    the input cheap to draw; every code and scale is compared."""
+    rng = np.random.default_rng(4000 + P)
+    n = 2 * 16384 * 1024 + 5 * 512 + 77
+    nb = -(-n // block)
+    codes = [rng.integers(0, 256, size=(n + 1) // 2, dtype=np.uint8) for _ in range(P)]
+    for c in codes:
+        c[-1] &= 0x0F
+    scales = [(rng.random(nb) * 1e-3 + 1e-7).astype(np.float32) for _ in range(P)]
+    _, rqc_o, rqs_o = O.dequant_reduce(codes, scales, n, block, 1.0, want_out=False, requant=True,
+                                       rq_ef=None, rq_beta_e=0.0, rq_beta_r=1.0)
+    rqc = Guarded((n + 1) // 2, torch.uint8)
+    rqs = Guarded(nb, torch.float32)
+    Z().zq_dequant_reduce([to_gpu(c) for c in codes], [to_gpu(s) for s in scales], n, block, 1.0,
+                          rq_codes=rqc.t, rq_scales=rqs.t)
+    torch.cuda.synchronize()
+    what = f"requant P={P} B={block} n={n}"
+    assert_bits_equal(rqc.host(), rqc_o, what + " codes")
+    assert_bits_equal(rqs.host(), rqs_o, what + " scales")
+
+
 # ----------------------------------------- batched dequantize + reduce --
 
 def _dr_segments(P, block, sizes, seed, raw):
