@@ -136,6 +136,31 @@ def test_binding_guards_reject_short_or_host_buffers():
                                torch.zeros(1))
 
 
+def test_binding_refuses_a_segment_table_used_with_other_sizes():
+    """A marshalled table's buffers were checked for its own P and block;
+    a call with another P or block would let the kernels index past them,
+    so the binding refuses it before calling the library.  The fake
+    pointers are misaligned as well, so the C ABI would refuse them too."""
+    odd = FAKE + 4
+    dr = zq.DrSegmentTable([(odd, odd + 0x100000, 4096, 2048, 32, odd + 0x200000, None, None,
+                             None)], P=4, block=128)
+    with pytest.raises(ValueError, match="P=4, block=128"):
+        zq.zq_dequant_reduce_batched(dr, 8, 128, 1.0)
+    with pytest.raises(ValueError, match="P=4, block=128"):
+        zq.zq_dequant_reduce_batched(dr, 4, 64, 1.0)
+    with pytest.raises(zq.ZQError, match="ALIGN"):  # same sizes: the C ABI's own checks run
+        zq.zq_dequant_reduce_batched(dr, 4, 128, 1.0, stream=0)
+    # an EF-quantize table of 4096 elements at block 256 (raw pointers)
+    efq = zq.EfqSegmentTable.__new__(zq.EfqSegmentTable)
+    efq.segments = [None]
+    efq.arr = (zq.EfqSegment * 1)(zq.EfqSegment(odd, None, odd + 0x100000, odd + 0x200000, 4096))
+    efq.dtype, efq.block, efq.ptr = zq.ZQ_FP32, 256, C.cast(efq.arr, C.c_void_p)
+    with pytest.raises(ValueError, match="block 256"):
+        zq.zq_quantize_ef_int4_batched(efq, 128, 1.0, 1.0)
+    with pytest.raises(zq.ZQError, match="ALIGN"):
+        zq.zq_quantize_ef_int4_batched(efq, 256, 1.0, 1.0, stream=0)
+
+
 def test_sr_batched_validation():
     Seg = zq.SrSegment
 

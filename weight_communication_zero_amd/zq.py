@@ -141,6 +141,9 @@ def _need(name: str, t, numel: int, dtypes) -> None:
         return
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
     if not t.is_contiguous():
@@ -321,6 +324,8 @@ def zq_quantize_ef_int4_batched(segments, block: int, beta_e: float, beta_r: flo
     """Per-tensor EF int4 quantize of many tensors in one call: `segments` is
     an EfqSegmentTable or an iterable of (g, ef or None, codes, scales)."""
     table = segments if isinstance(segments, EfqSegmentTable) else EfqSegmentTable(segments, block)
+    if table.block != block:
+        raise ValueError(f"the segment table was checked for block {table.block}, not {block}")
     _check("zq_quantize_ef_int4_batched",
            lib.zq_quantize_ef_int4_batched(table.ptr, len(table.segments),
                                            ZQ_FP32 if table.dtype is None else table.dtype, block,
@@ -356,6 +361,9 @@ def zq_dequant_reduce_batched(segments, P: int, block: int, alpha: float, rq_bet
     """Per-tensor dequantize-reduce(-requant) of many tensors in one call:
     `segments` is a DrSegmentTable or an iterable of its tuples."""
     table = segments if isinstance(segments, DrSegmentTable) else DrSegmentTable(segments, P, block)
+    if (table.P, table.block) != (P, block):
+        raise ValueError(f"the segment table was checked for P={table.P}, block={table.block}, "
+                         f"not P={P}, block={block}")
     _check("zq_dequant_reduce_batched",
            lib.zq_dequant_reduce_batched(table.ptr, len(table.segments), P, block, alpha, rq_beta_e,
                                          rq_beta_r, _stream(stream)))
