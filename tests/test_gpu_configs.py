@@ -514,3 +514,75 @@ def test_per_tensor_batched_reduce_requant_7p5b_sampled():
         assert_bits_equal(int4_block_bytes(rqc, out_blocks, B), rc_o, what + " requant codes")
         assert_bits_equal(to_host(rqs)[out_blocks], rs_o, what + " requant scales")
         assert_bits_equal(gather_blocks(rq_ef, out_blocks, B), rq_ef_o, what + " requant ef")
+
+
+# ------------------- the 7.5B send side in ZeRO++ order and per parameter --
+
+def test_send_side_forms_7p5b_equal_the_flat_call():
+    """The benchmark's other two EF-quantize forms at their full 7.5B size,
+    each against the flat call from the same EF state: the ZeRO++ order for
+    4 nodes of 8 GPUs ("ZeROPlusPlus.md" notes, section 1.2) must hold
+    partition p's codes and scales in slot sigma(p) and leave the EF buffer
+    exactly as the flat call does; the per-parameter call over the 327
+    tensors ("Merge LoCo with Zero++", review thread) must equal the flat
+    call everywhere.  The first and last block of every partition are also
+    checked against the oracle from host copies of g and the EF state."""
+    tensors = synth.llama_7p5b()
+    M = synth.total(tensors)
+    B, intra, inter = 128, 8, 4
+    n_part = intra * inter
+    part = M // n_part
+    g = torch.empty(M, dtype=torch.float32, device="cuda")
+    synth.fill_model(g, tensors, std=1e-3, seed=synth.seed_for("llama7p5b", "grad", step=0),
+                     heavy_tails=True)
+    ef_flat = torch.empty(M, dtype=torch.float32, device="cuda")
+    ef_w = torch.empty(M, dtype=torch.float32, device="cuda")
+    ef_seed = synth.seed_for("llama7p5b", "ef")
+    synth.fill_model(ef_flat, None, std=1e-5, seed=ef_seed)
+    blocks = np.array(sorted({p * part // B for p in range(n_part)} |
+                             {(p + 1) * part // B - 1 for p in range(n_part)}))
+    g_h = gather_blocks(g, blocks, B)
+    e_h = gather_blocks(ef_flat, blocks, B)
+    c_flat = torch.empty(M // 2, dtype=torch.uint8, device="cuda")
+    s_flat = torch.empty(M // B, dtype=torch.float32, device="cuda")
+    Z().zq_quantize_ef_int4(g, ef_flat, B, 0.9, 1.0, c_flat, s_flat)
+
+    c_w = torch.full((M // 2,), 0x88, dtype=torch.uint8, device="cuda")
+    s_w = torch.full((M // B,), float("nan"), device="cuda")
+    synth.fill_model(ef_w, None, std=1e-5, seed=ef_seed)
+    slots = Z().zeropp_slots(intra, inter)
+    Z().zq_quantize_ef_int4_permuted(g, ef_w, B, 0.9, 1.0, c_w, s_w, slots)
+    torch.cuda.synchronize()
+    assert torch.equal(ef_w.view(torch.int32), ef_flat.view(torch.int32)), "permuted: EF differs"
+    for p in range(n_part):
+        q = slots[p]
+        assert torch.equal(c_w[q * part // 2:(q + 1) * part // 2],
+                           c_flat[p * part // 2:(p + 1) * part // 2]), f"partition {p} codes"
+        assert torch.equal(s_w[q * part // B:(q + 1) * part // B].view(torch.int32),
+                           s_flat[p * part // B:(p + 1) * part // B].view(torch.int32)), \
+            f"partition {p} scales"
+    c_o, s_o = O.quantize_ef_int4(g_h, e_h, B, 0.9, 1.0)
+    for i, b in enumerate(blocks):
+        p, r = divmod(int(b), part // B)
+        slot_block = slots[p] * (part // B) + r
+        assert_bits_equal(to_host(c_w[slot_block * B // 2:(slot_block + 1) * B // 2]),
+                          c_o[i * B // 2:(i + 1) * B // 2], f"permuted block {b} codes")
+        assert_bits_equal(to_host(s_w[slot_block:slot_block + 1]), s_o[i:i + 1],
+                          f"permuted block {b} scale")
+        assert_bits_equal(to_host(ef_w[b * B:(b + 1) * B]), e_h[i * B:(i + 1) * B],
+                          f"block {b} EF")
+
+    c_w.fill_(0x88)
+    s_w.fill_(float("nan"))
+    synth.fill_model(ef_w, None, std=1e-5, seed=ef_seed)
+    segs, off = [], 0
+    for t in tensors:
+        n = t.numel
+        segs.append((g[off:off + n], ef_w[off:off + n], c_w[off // 2:(off + n) // 2],
+                     s_w[off // B:(off + n) // B]))
+        off += n
+    Z().zq_quantize_ef_int4_batched(segs, B, 0.9, 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(c_w, c_flat), "per-parameter codes differ from the flat call"
+    assert torch.equal(s_w.view(torch.int32), s_flat.view(torch.int32)), "per-parameter scales"
+    assert torch.equal(ef_w.view(torch.int32), ef_flat.view(torch.int32)), "per-parameter EF"
