@@ -457,8 +457,9 @@ def test_per_tensor_batched_reduce_requant_7p5b_sampled():
     """The receive side parameter by parameter over the ~7.5B model's 327
     tensors: tensor i's receive buffer holds its 8 peer chunks of n_i / 8
     elements (contiguous, as an all-to-all delivers them), each reduced and
-    requantized on its own with its own requant EF buffer, 2 steps -- one
-    zq_dequant_reduce_batched call per step.  Whole outputs poisoned and
+    requantized on its own with its own requant EF buffer, 2 steps, then a
+    third step without requant EF -- one zq_dequant_reduce_batched call per
+    step.  Whole outputs poisoned and
     checked written; the first and last output block of every tensor and
     random others recomputed by the oracle from the generator's inputs."""
     tensors = synth.llama_7p5b()
@@ -481,6 +482,7 @@ def test_per_tensor_batched_reduce_requant_7p5b_sampled():
         off += t.numel
         roff += m
     table = Z().DrSegmentTable(segs, P, B)
+    table_noef = Z().DrSegmentTable([sg[:8] + (None,) for sg in segs], P, B)
     rng = np.random.default_rng(21)
     # tracked output blocks: (segment, block within the segment)
     picks = []
@@ -492,15 +494,19 @@ def test_per_tensor_batched_reduce_requant_7p5b_sampled():
     out_blocks = np.array([where[i][1] // B + b for i, b in picks])
     in_blocks = np.array([(where[i][0] + j * where[i][2]) // B + b for i, b in picks for j in range(P)])
     rq_ef_o = np.zeros(out_blocks.size * B, np.float32)
-    for step in range(2):
+    for step in range(3):
+        # steps 0 and 1 with the per-tensor requant EF buffers, step 2 without
+        # (the benchmark's batched requant row)
+        with_ef = step < 2
         synth.fill_model(g, tensors, std=1e-3, seed=synth.seed_for("llama7p5b", "grad", step=step),
                          heavy_tails=True)
         Z().zq_quantize_ef_int4(g, None, B, 0.0, 1.0, codes, scales)
         rqc.fill_(0x88)
         rqs.fill_(float("nan"))
-        Z().zq_dequant_reduce_batched(table, P, B, 1.0, rq_beta_e=0.9, rq_beta_r=1.0)
+        Z().zq_dequant_reduce_batched(table if with_ef else table_noef, P, B, 1.0,
+                                      rq_beta_e=0.9, rq_beta_r=1.0)
         torch.cuda.synchronize()
-        what = f"7.5B per-tensor reduce step {step}"
+        what = f"7.5B per-tensor reduce step {step} ({'with' if with_ef else 'no'} requant EF)"
         assert not bool(((rqc & 0x0F) == 8).any() | ((rqc >> 4) == 8).any()), what + ": codes unwritten"
         assert not bool(torch.isnan(rqs).any()), what + ": scales unwritten"
         # oracle: the 8 input blocks of every tracked output block, in order
@@ -510,7 +516,8 @@ def test_per_tensor_batched_reduce_requant_7p5b_sampled():
               for j in range(P)]
         sj = [np.array([s0[q * P + j] for q in range(k)], np.float32) for j in range(P)]
         _, rc_o, rs_o = O.dequant_reduce(cj, sj, k * B, B, 1.0, want_out=False, requant=True,
-                                         rq_ef=rq_ef_o, rq_beta_e=0.9, rq_beta_r=1.0)
+                                         rq_ef=rq_ef_o if with_ef else None, rq_beta_e=0.9,
+                                         rq_beta_r=1.0)
         assert_bits_equal(int4_block_bytes(rqc, out_blocks, B), rc_o, what + " requant codes")
         assert_bits_equal(to_host(rqs)[out_blocks], rs_o, what + " requant scales")
         assert_bits_equal(gather_blocks(rq_ef, out_blocks, B), rq_ef_o, what + " requant ef")
