@@ -35,10 +35,12 @@
  *   - Inputs are expected finite.  A NaN or infinity inside a block makes
  *     that block's scale non-finite; results for it are defined by the same
  *     arithmetic but are outside the supported contract.
- *   - Arithmetic is IEEE binary32, round to nearest even, no fused
- *     multiply-add, denormals kept; integer codes, scales (as bits), error-
- *     feedback buffers and bf16 / fp16 outputs are bit-exact functions of the
- *     inputs.
+ *   - Results are defined by IEEE binary32 arithmetic, round to nearest
+ *     even, no fused multiply-add, denormals kept, applied in the order each
+ *     formula below is written (the kernels may take other instruction
+ *     sequences, e.g. fused ones, only where they give the same bits);
+ *     integer codes, scales (as bits), error-feedback buffers and bf16 / fp16
+ *     outputs are bit-exact functions of the inputs.
  *
  * Layouts
  *   int4 codes: two's-complement nibbles, element 2j in the low nibble of
