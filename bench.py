@@ -324,6 +324,13 @@ def variant_rows(torch, zq, g, ef, codes, scales, chunks_c, chunks_s, rq_codes, 
                                                         rq_ef=rq_ef, rq_beta_e=beta,
                                                         rq_beta_r=1.0), 10)
     del rq_ef
+    # half-precision gradients (the LoCo kernel loads half values), same EF buffer
+    half_ms = {}
+    for name, dt in (("bf16", torch.bfloat16), ("fp16", torch.float16)):
+        gh = g.to(dt)
+        half_ms[name] = timed(torch, lambda: zq.zq_quantize_ef_int4(gh, ef, B, beta, 1.0, codes,
+                                                                    scales), 10)
+        del gh
     # ZeRO++ hierarchical order (4 nodes x 8 GPUs): EF quantize into permuted partitions
     slots = zq.zeropp_slots(P1, P2)
     ms_perm = timed(torch, lambda: zq.zq_quantize_ef_int4_permuted(g, ef, B, beta, 1.0, codes,
@@ -373,6 +380,8 @@ def variant_rows(torch, zq, g, ef, codes, scales, chunks_c, chunks_s, rq_codes, 
         "efq_batched_327_tensors_fp32_b128_7.5B": dict(row(bytes_efq, ms_batched, M),
                                                        host_enqueue_ms=round(host_efqb, 4)),
         "efq_permuted_zeropp_4x8_fp32_b128_7.5B": row(bytes_efq, ms_perm, M),
+        "efq_bf16_b128_7.5B": row(efq_bytes(M, B, 2), half_ms["bf16"], M),
+        "efq_fp16_b128_7.5B": row(efq_bytes(M, B, 2), half_ms["fp16"], M),
         "dequant_reduce_requant_ef_p8_b128_7.5B": row(
             dr_bytes(n1, B, P1, out=False, rq=True, rq_ef=True), ms_rqef, n1),
     }

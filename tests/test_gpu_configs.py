@@ -593,3 +593,34 @@ def test_send_side_forms_7p5b_equal_the_flat_call():
     assert torch.equal(c_w, c_flat), "per-parameter codes differ from the flat call"
     assert torch.equal(s_w.view(torch.int32), s_flat.view(torch.int32)), "per-parameter scales"
     assert torch.equal(ef_w.view(torch.int32), ef_flat.view(torch.int32)), "per-parameter EF"
+
+
+def test_efq_bf16_gradients_7p5b_sampled():
+    """The EF quantizer on the 7.5B gradient in bf16 (half-precision
+    gradients, as the LoCo kernel loads them, "Merge LoCo with Zero++",
+    review thread) with an fp32 EF buffer, the benchmark's bf16 row: every
+    code and scale written, the first and last block and 254 random ones
+    (codes, scales, updated EF) against the oracle."""
+    tensors = synth.llama_7p5b()
+    M = synth.total(tensors)
+    B = 128
+    g = torch.empty(M, dtype=torch.bfloat16, device="cuda")
+    synth.fill_model(g, tensors, std=1e-3, seed=synth.seed_for("llama7p5b", "grad", step=1),
+                     heavy_tails=True)
+    ef = torch.empty(M, dtype=torch.float32, device="cuda")
+    synth.fill_model(ef, None, std=1e-5, seed=synth.seed_for("llama7p5b", "ef"))
+    nb = M // B
+    rng = np.random.default_rng(31)
+    blocks = np.unique(np.concatenate([[0, nb - 1], rng.integers(0, nb, size=254)]))
+    g_h = gather_blocks(g, blocks, B)
+    e_h = gather_blocks(ef, blocks, B)
+    codes = torch.full((M // 2,), 0x88, dtype=torch.uint8, device="cuda")
+    scales = torch.full((nb,), float("nan"), device="cuda")
+    Z().zq_quantize_ef_int4(g, ef, B, 0.9, 1.0, codes, scales)
+    torch.cuda.synchronize()
+    assert not bool(((codes & 0x0F) == 8).any() | ((codes >> 4) == 8).any()), "codes unwritten"
+    assert not bool(torch.isnan(scales).any()), "scales unwritten"
+    c_o, s_o = O.quantize_ef_int4(g_h, e_h, B, 0.9, 1.0)
+    assert_bits_equal(int4_block_bytes(codes, blocks, B), c_o, "bf16 7.5B codes")
+    assert_bits_equal(to_host(scales)[blocks], s_o, "bf16 7.5B scales")
+    assert_bits_equal(gather_blocks(ef, blocks, B), e_h, "bf16 7.5B EF")
