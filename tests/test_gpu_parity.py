@@ -217,6 +217,19 @@ def test_dequant_reduce_requant(block, flags):
         check_dr(P, n, block, 1.0, want_out, requant, rqef, seed=7 * block + i)
 
 
+@pytest.mark.parametrize("block", [64, 4096])
+@pytest.mark.parametrize("with_rq_ef", [False, True])
+@pytest.mark.parametrize("P", range(1, 17))
+def test_requant_every_peer_count(block, with_rq_ef, P):
+    """The requant flavours for every peer count 1..16: the kernels are
+    compiled for at most 2, 4, 8 and 16 peers and skip the unused ones at
+    run time, so each count exercises a different number of live peers in
+    its instantiation.  Blocks inside one sub-vector (64) and spanning
+    several (4096); a ragged last tile; quantized gradients, not raw."""
+    n = max(1024, block) * 3 + 17
+    check_dr(P, n, block, 1.0 / P, False, True, with_rq_ef, seed=90 * P + block + with_rq_ef)
+
+
 @pytest.mark.parametrize("alpha", [1.0, 0.25, 1.0 / 3.0, -2.0])
 def test_dequant_reduce_alpha_and_raw_codes(alpha):
     check_dr(6, 4096 * 3 + 5, 128, alpha, True, True, True, seed=11, raw=True)
