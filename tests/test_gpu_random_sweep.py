@@ -35,7 +35,7 @@ def _size(rng, block):
 DTYPES = ["fp32", "bf16", "fp16"]
 
 
-@pytest.mark.parametrize("case", range(24))
+@pytest.mark.parametrize("case", range(64))
 def test_efq_random_configs(case):
     rng = np.random.default_rng(1000 + case)
     block = int(rng.choice(BLOCKS))
@@ -51,7 +51,7 @@ def test_efq_random_configs(case):
               f"random efq case={case} n={n} B={block} {gdt} ef={with_ef} beta=({be},{br})")
 
 
-@pytest.mark.parametrize("case", range(16))
+@pytest.mark.parametrize("case", range(64))
 def test_dequant_reduce_random_configs(case):
     rng = np.random.default_rng(4000 + case)
     block = int(rng.choice(BLOCKS))
@@ -64,7 +64,7 @@ def test_dequant_reduce_random_configs(case):
     check_dr(P, n, block, alpha, *flags, seed=5000 + case, raw=raw)
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(32))
 def test_int8_random_configs(case):
     rng = np.random.default_rng(6000 + case)
     block = int(rng.choice(BLOCKS))
@@ -89,7 +89,7 @@ def test_int8_random_configs(case):
     assert_bits_equal(out.host(), o_o, what + f" dequant to {odt}")
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(32))
 def test_sr_random_configs(case):
     rng = np.random.default_rng(8000 + case)
     n = _size(rng, 1024)
