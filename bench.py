@@ -15,7 +15,9 @@ value = algorithmic bytes of one step / measured step time (inputs resident
 in HBM).  The same run also times the other kernels of the path on their own
 workloads (int8 weight quantize/dequantize of a ~0.85B model, stochastic-
 rounding accumulation of GPT-2 124M gradients, the 0.85B EF-quantize + 8-way
-reduce, the 4-rank bf16 case) and the CPU oracle on a bounded sample.
+reduce, the 4-rank bf16 case), the step's variants at 7.5B (requant EF, bf16
+and fp16 gradients, the ZeRO++ partition order, the per-parameter batched
+calls) and the CPU oracle on a bounded sample.
 """
 from __future__ import annotations
 
