@@ -14,12 +14,13 @@ constexpr uint32_t kMaxPeers = 16;
 // Element types of the 16- and 32-bit data streams (the values of zq_dtype).
 enum ElemType : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
 
-// Launch geometry of a streaming kernel: threads per workgroup (64..256)
-// and the most workgroups one launch may have; a larger job walks its tiles
-// with a grid stride.  Measured on MI355X: one-tile-per-wave grids of 1-wave
-// workgroups stream best (the dispatcher keeps every CU fed and a wave never
-// waits on a sibling), except for the ALU-heavy reduce+requant, which runs
-// best persistent (4096 workgroups of 4 waves walking many tiles).
+// Launch geometry of a kernel: threads per workgroup (64..256) and the most
+// workgroups one launch may have; a larger job walks its tiles with a grid
+// stride.  Measured on MI355X: the streaming kernels run best with one tile
+// per wave in 1-wave workgroups (the dispatcher keeps every CU fed and a
+// wave never waits on a sibling), the reduces with one tile per wave in
+// 4-wave workgroups, and the ALU-heavy reduce+requant without EF persistent
+// (4096 workgroups of 4 waves walking many tiles).
 struct Geometry {
     uint32_t threads;
     uint32_t max_wgs;

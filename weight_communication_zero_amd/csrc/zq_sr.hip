@@ -135,10 +135,11 @@ const void* sr_pick(uint64_t counter_base, bool zero) {
 // Batched segments: one launch runs the SR tiles of up to kSegsPerLaunch
 // segments and, with zero_src, the tiles that clear the rest of each
 // segment's source buffer.  The table (with cumulative tile counts) travels
-// in the kernel arguments; a wave finds its segment by a uniform scan.
-// Fewer launches pay: GPT-2's 148 tensors took 91 / 75.5 / 71 us with 16 /
-// 32 / 50 segments per launch (MI355X); 50 keeps the table (3.2 KB) inside
-// the 4 KB kernel-argument space.
+// in the kernel arguments; a wave finds its segment from the cumulative
+// counts, held one per lane (SegmentFinder).  Fewer launches pay: GPT-2's
+// 148 tensors took 91 / 75.5 / 71 us with 16 / 32 / 50 segments per launch
+// (MI355X, with the earlier per-entry scalar search); 50 keeps the table
+// (3.2 KB) inside the 4 KB kernel-argument space.
 #ifndef ZQ_SR_SEGS
 #define ZQ_SR_SEGS 50
 #endif
