@@ -61,7 +61,11 @@
 extern "C" {
 #endif
 
-#define ZQ_ABI_VERSION 1u
+/* 1: the single-call entry points (the permuted quantize included) and the
+ *    batched SR and EF quantize;
+ * 2: adds ZQ_FP16, zq_zeropp_slots and zq_dequant_reduce_batched (earlier
+ *    calls and layouts unchanged). */
+#define ZQ_ABI_VERSION 2u
 
 typedef enum {
     ZQ_OK = 0,

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_host_helpers():
-    assert L.zq_abi_version() == 1
+    assert L.zq_abi_version() == 2
     for n in [0, 1, 2, 3, 4095, 2 ** 33 + 1]:
         assert L.zq_int4_code_bytes(n) == (n + 1) // 2
         for b in [32, 128, 4096]:
