@@ -39,14 +39,14 @@ def test_threads_on_their_own_streams_match_one_thread():
     def run(stream, job):
         try:
             torch.cuda.set_device(0)
-            start.wait()
+            start.wait(timeout=60)
             with torch.cuda.stream(stream):
                 for _ in range(rounds):
                     job()
         except BaseException as e:  # reported by the main thread
             errors.append(e)
 
-    threads = [threading.Thread(target=run, args=(st, job))
+    threads = [threading.Thread(target=run, args=(st, job), daemon=True)
                for st, job in zip(streams, jobs(zq, A))]
     for t in threads:
         t.start()
